@@ -1,0 +1,217 @@
+"""MI355X (gfx950) MosaicQuant library: Python binding over the C ABI in include/mq.h.
+
+The functions below only marshal torch device tensors (pointers, sizes and the
+current HIP stream) into ``libmq.so``; every step of the computation runs in the
+library's HIP kernels. There is no CPU fallback: importing this package raises
+if the library has not been built (``python -m dense_sparse_bit_amd._build``),
+and every call raises :class:`MQError` on a non-zero status.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch  # loads torch's HIP runtime first, so libmq.so binds to the same one
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmq.so")
+
+MQ_F32, MQ_BF16 = 0, 1
+GROUP, BK = 128, 64
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m dense_sparse_bit_amd._build` "
+                      "(hipcc, gfx950). There is no fallback implementation.")
+
+_lib = C.CDLL(LIB_PATH)
+_p, _i64, _int = C.c_void_p, C.c_int64, C.c_int
+
+_SIGS = {
+    "mq_hessian_diag": [_p, _int, _i64, _i64, _p, _p],
+    "mq_quantize_act": [_p, _int, _i64, _i64, _p, _p, _p],
+    "mq_select_blocks": [_p, _p, _i64, _i64, _int, _int, _int, _i64, _p, _p, _p, _p],
+    "mq_pack_weights": [_p, _i64, _i64, _int, _int, _int, _p, _p, _i64, _p, _p, _p, _p],
+    "mq_gemm_w4a4_residual": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
+                              _p, _int, _p, _p],
+    "mq_gemm_w4a4_dense": [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p, _int, _p, _p],
+    "mq_gemm_residual_separate": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int,
+                                  _int, _p, _int, _p, _p],
+}
+for _name, _args in _SIGS.items():
+    getattr(_lib, _name).argtypes = _args
+    getattr(_lib, _name).restype = C.c_int
+_lib.mq_status_string.argtypes = [C.c_int]
+_lib.mq_status_string.restype = C.c_char_p
+_lib.mq_version.argtypes = []
+_lib.mq_version.restype = C.c_int
+
+EXPORTS = tuple(_SIGS) + ("mq_status_string", "mq_version")
+
+
+class MQError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def status_string(status: int) -> str:
+    return _lib.mq_status_string(status).decode()
+
+
+def version() -> int:
+    return int(_lib.mq_version())
+
+
+def lib():
+    """The loaded ctypes library (raw C ABI)."""
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _call(fn: str, *args):
+    rc = getattr(_lib, fn)(*args)
+    if rc != 0:
+        raise MQError(fn, rc)
+
+
+def _x_dtype(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return MQ_F32
+    if x.dtype == torch.bfloat16:
+        return MQ_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {x.dtype}")
+
+
+def _device_contig(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# --------------------------------------------------------------------------- a0
+def hessian_diag(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    _device_contig(x, "x")
+    M, K = x.shape
+    h = torch.empty(K, dtype=torch.float32, device=x.device) if out is None else out
+    _call("mq_hessian_diag", _ptr(x), _x_dtype(x), M, K, _ptr(h), _stream(stream))
+    return h
+
+
+# --------------------------------------------------------------------------- a4
+def quantize_act(x: torch.Tensor, xq: torch.Tensor | None = None, sx: torch.Tensor | None = None,
+                 stream=None):
+    _device_contig(x, "x")
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if sx is None:
+        sx = torch.empty(M, dtype=torch.float32, device=x.device)
+    _call("mq_quantize_act", _ptr(x), _x_dtype(x), M, K, _ptr(xq), _ptr(sx), _stream(stream))
+    return xq, sx
+
+
+# --------------------------------------------------------------------------- a2
+def select_blocks(w: torch.Tensor, h: torch.Tensor, k_blocks: int, bn: int = 64, group: int = GROUP,
+                  bk: int = BK, out=None, stream=None):
+    """Returns (row_ptr int32 [N/bn+1], col_idx int32 [k_blocks], delta fp64 [NB])."""
+    _device_contig(w, "w")
+    _device_contig(h, "h")
+    N, K = w.shape
+    nb = (N // bn) * (K // bk)
+    if out is None:
+        row_ptr = torch.empty(N // bn + 1, dtype=torch.int32, device=w.device)
+        col_idx = torch.empty(max(k_blocks, 1), dtype=torch.int32, device=w.device)
+        delta = torch.empty(max(nb, 1), dtype=torch.float64, device=w.device)
+    else:
+        row_ptr, col_idx, delta = out
+    _call("mq_select_blocks", _ptr(w), _ptr(h), N, K, group, bn, bk, k_blocks, _ptr(row_ptr),
+          _ptr(col_idx), _ptr(delta), _stream(stream))
+    return row_ptr, col_idx[:k_blocks], delta[:nb]
+
+
+# --------------------------------------------------------------------------- a1 + a3
+def pack_weights(w: torch.Tensor, row_ptr: torch.Tensor, col_idx: torch.Tensor, bn: int = 64,
+                 group: int = GROUP, bk: int = BK, out=None, stream=None):
+    """Returns (wq u8 [N][K/2], sw fp16-bits int16 [N][K/group], rq u8 [nnz][bn][bk/2])."""
+    _device_contig(w, "w")
+    N, K = w.shape
+    nnz = int(col_idx.numel())
+    if out is None:
+        wq = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+        sw = torch.empty((N, K // group), dtype=torch.int16, device=w.device)
+        rq = torch.empty((max(nnz, 1), bn, bk // 2), dtype=torch.uint8, device=w.device)
+    else:
+        wq, sw, rq = out
+    _call("mq_pack_weights", _ptr(w), N, K, group, bn, bk, _ptr(row_ptr),
+          _ptr(col_idx) if nnz else None, nnz, _ptr(wq), _ptr(sw), _ptr(rq) if nnz else None,
+          _stream(stream))
+    return wq, sw, rq[:nnz]
+
+
+# --------------------------------------------------------------------------- a5..a10
+def _y_dtype(dtype) -> int:
+    if dtype == torch.float32:
+        return MQ_F32
+    if dtype == torch.bfloat16:
+        return MQ_BF16
+    raise TypeError(f"output must be float32 or bfloat16, got {dtype}")
+
+
+def gemm_w4a4_residual(xq, sx, wq, sw, row_ptr, col_idx, rq, K: int, bn: int = 64,
+                       out_dtype=torch.bfloat16, y=None, acc_dump=None, stream=None):
+    """Fused dense + sparse-residual W4A4 GEMM. acc_dump: optional int32 [M][N][K/128]."""
+    M, N = xq.shape[0], wq.shape[0]
+    nnz = int(col_idx.numel())
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=wq.device)
+    _call("mq_gemm_w4a4_residual", _ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(row_ptr),
+          _ptr(col_idx) if nnz else None, _ptr(rq) if nnz else None, nnz, M, N, K, GROUP, bn, BK,
+          _ptr(y), _y_dtype(y.dtype), _ptr(acc_dump), _stream(stream))
+    return y
+
+
+def gemm_w4a4_dense(xq, sx, wq, sw, K: int, out_dtype=torch.bfloat16, y=None, acc_dump=None,
+                    stream=None):
+    M, N = xq.shape[0], wq.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=wq.device)
+    _call("mq_gemm_w4a4_dense", _ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, GROUP, _ptr(y),
+          _y_dtype(y.dtype), _ptr(acc_dump), _stream(stream))
+    return y
+
+
+def gemm_residual_separate(xq, sx, wq, sw, row_ptr, col_idx, rq, K: int, bn: int = 64,
+                           out_dtype=torch.bfloat16, y=None, ws=None, stream=None):
+    M, N = xq.shape[0], wq.shape[0]
+    nnz = int(col_idx.numel())
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=wq.device)
+    if ws is None:
+        ws = torch.empty((M, N), dtype=torch.float32, device=wq.device)
+    _call("mq_gemm_residual_separate", _ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(row_ptr),
+          _ptr(col_idx) if nnz else None, _ptr(rq) if nnz else None, nnz, M, N, K, GROUP, bn, BK,
+          _ptr(y), _y_dtype(y.dtype), _ptr(ws), _stream(stream))
+    return y
+
+
+def forward_layer(x, w, k_blocks: int, bn: int = 64, out_dtype=torch.bfloat16, stream=None):
+    """The whole path on device: h -> select -> pack -> quantize X -> fused GEMM."""
+    h = hessian_diag(x, stream=stream)
+    row_ptr, col_idx, delta = select_blocks(w, h, k_blocks, bn=bn, stream=stream)
+    wq, sw, rq = pack_weights(w, row_ptr, col_idx, bn=bn, stream=stream)
+    xq, sx = quantize_act(x, stream=stream)
+    y = gemm_w4a4_residual(xq, sx, wq, sw, row_ptr, col_idx, rq, w.shape[1], bn=bn,
+                           out_dtype=out_dtype, stream=stream)
+    return dict(h=h, row_ptr=row_ptr, col_idx=col_idx, delta=delta, wq=wq, sw=sw, rq=rq, xq=xq,
+                sx=sx, y=y)

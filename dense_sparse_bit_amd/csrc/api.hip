@@ -1,0 +1,176 @@
+// C ABI of the MosaicQuant library: argument checks, then kernel launches.
+// Declarations and the meaning of every argument are in include/mq.h.
+#include <stdint.h>
+
+#include "../../include/mq.h"
+#include "mq_device.h"
+#include "mq_internal.h"
+
+namespace {
+
+constexpr int kVersion = 10000;   // 1.0.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MQ_OK : MQ_ERR_HIP; }
+
+bool bad_dtype(int d) { return d != MQ_F32 && d != MQ_BF16; }
+
+// shapes the GPU path supports (see mq.h)
+int check_layer(int64_t N, int64_t K, int group, int bn, int bk) {
+    if (N <= 0 || K <= 0) return MQ_ERR_INVALID_ARG;
+    if (group != mq::kGroup || bk != mq::kBk || (bn != 64 && bn != 128)) return MQ_ERR_UNSUPPORTED;
+    if (K % mq::kGroup || N % bn) return MQ_ERR_UNSUPPORTED;
+    if (K > (int64_t(1) << 30) || N > (int64_t(1) << 30) || N * K > (int64_t(1) << 40))
+        return MQ_ERR_UNSUPPORTED;
+    return MQ_OK;
+}
+
+int check_gemm(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint16_t* sw, int64_t M,
+               int64_t N, int64_t K, int group, int bn, int bk, const void* y, int y_dtype) {
+    int rc = check_layer(N, K, group, bn, bk);
+    if (rc) return rc;
+    if (M < 0 || M > (int64_t(1) << 24)) return MQ_ERR_INVALID_ARG;
+    if (bad_dtype(y_dtype)) return MQ_ERR_INVALID_ARG;
+    if (M > 0 && (!xq || !sx || !y)) return MQ_ERR_INVALID_ARG;
+    if (!wq || !sw) return MQ_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(wq)) return MQ_ERR_INVALID_ARG;
+    // every int32 index the kernels form must fit
+    if (M * N > (int64_t(1) << 31) - 1 || M * N * (K / mq::kGroup) > (int64_t(1) << 40))
+        return MQ_ERR_UNSUPPORTED;
+    return MQ_OK;
+}
+
+int check_csr(const int32_t* row_ptr, const int32_t* col_idx, const uint8_t* rq, int64_t nnz,
+              int64_t N, int64_t K, int bn, int bk) {
+    if (nnz < 0 || nnz > (N / bn) * (K / bk)) return MQ_ERR_INVALID_ARG;
+    if (!row_ptr) return MQ_ERR_INVALID_ARG;
+    if (nnz > 0 && (!col_idx || !rq || !aligned16(rq))) return MQ_ERR_INVALID_ARG;
+    return MQ_OK;
+}
+
+mq::GemmArgs make_args(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint16_t* sw,
+                       const int32_t* row_ptr, const int32_t* col_idx, const uint8_t* rq,
+                       int64_t nnz, int64_t M, int64_t N, int64_t K, int bn, void* y, int y_dtype,
+                       int32_t* acc_dump, float* ws) {
+    mq::GemmArgs a;
+    a.xq = xq;
+    a.sx = sx;
+    a.wq = wq;
+    a.sw = sw;
+    a.row_ptr = row_ptr;
+    a.col_idx = col_idx;
+    a.rq = rq;
+    a.nnz = static_cast<int>(nnz);
+    a.M = static_cast<int>(M);
+    a.N = static_cast<int>(N);
+    a.K = static_cast<int>(K);
+    a.bn = bn;
+    a.y = y;
+    a.y_bf16 = y_dtype == MQ_BF16;
+    a.acc_dump = acc_dump;
+    a.ws = ws;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mq_status_string(int status) {
+    switch (status) {
+        case MQ_OK: return "ok";
+        case MQ_ERR_INVALID_ARG: return "invalid argument (null pointer, size, alignment or count)";
+        case MQ_ERR_UNSUPPORTED: return "unsupported shape (needs K % 128 == 0, group 128, bk 64, bn 64 or 128, N % bn == 0)";
+        case MQ_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int mq_version(void) { return kVersion; }
+
+int mq_hessian_diag(const void* x, int x_dtype, int64_t M, int64_t K, float* h, void* stream) {
+    if (M <= 0 || K <= 0 || !x || !h || bad_dtype(x_dtype)) return MQ_ERR_INVALID_ARG;
+    if (M * K > (int64_t(1) << 40)) return MQ_ERR_UNSUPPORTED;
+    return hip_status(mq::launch_hessian(x, x_dtype == MQ_BF16, M, K, h, static_cast<hipStream_t>(stream)));
+}
+
+int mq_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* xq, float* sx,
+                    void* stream) {
+    if (M < 0 || K <= 0 || (K & 1) || bad_dtype(x_dtype)) return MQ_ERR_INVALID_ARG;
+    if (M > (int64_t(1) << 31) - 1 || M * K > (int64_t(1) << 40)) return MQ_ERR_UNSUPPORTED;
+    if (M == 0) return MQ_OK;
+    if (!x || !xq || !sx) return MQ_ERR_INVALID_ARG;
+    return hip_status(mq::launch_quant_act(x, x_dtype == MQ_BF16, M, K, xq, sx, static_cast<hipStream_t>(stream)));
+}
+
+int mq_select_blocks(const float* w, const float* h, int64_t N, int64_t K, int group, int bn, int bk,
+                     int64_t k_blocks, int32_t* row_ptr, int32_t* col_idx, double* delta,
+                     void* stream) {
+    int rc = check_layer(N, K, group, bn, bk);
+    if (rc) return rc;
+    const int64_t nb = (N / bn) * (K / bk);
+    if (k_blocks < 0 || k_blocks > nb) return MQ_ERR_INVALID_ARG;
+    if (!w || !h || !row_ptr || !delta || (k_blocks > 0 && !col_idx) || !aligned16(w))
+        return MQ_ERR_INVALID_ARG;
+    return hip_status(mq::launch_select(w, h, N, K, bn, k_blocks, row_ptr, col_idx, delta,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int mq_pack_weights(const float* w, int64_t N, int64_t K, int group, int bn, int bk,
+                    const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz, uint8_t* wq,
+                    uint16_t* sw, uint8_t* rq, void* stream) {
+    int rc = check_layer(N, K, group, bn, bk);
+    if (rc) return rc;
+    if (!w || !wq || !sw || !aligned16(w)) return MQ_ERR_INVALID_ARG;
+    rc = check_csr(row_ptr, col_idx, rq, nnz, N, K, bn, bk);
+    if (rc) return rc;
+    return hip_status(mq::launch_pack(w, N, K, bn, row_ptr, col_idx, nnz, wq, sw, rq,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int mq_gemm_w4a4_residual(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint16_t* sw,
+                          const int32_t* row_ptr, const int32_t* col_idx, const uint8_t* rq,
+                          int64_t nnz, int64_t M, int64_t N, int64_t K, int group, int bn, int bk,
+                          void* y, int y_dtype, int32_t* acc_dump, void* stream) {
+    int rc = check_gemm(xq, sx, wq, sw, M, N, K, group, bn, bk, y, y_dtype);
+    if (rc) return rc;
+    rc = check_csr(row_ptr, col_idx, rq, nnz, N, K, bn, bk);
+    if (rc) return rc;
+    if (M == 0) return MQ_OK;
+    const mq::GemmArgs a = make_args(xq, sx, wq, sw, row_ptr, col_idx, rq, nnz, M, N, K, bn, y, y_dtype,
+                                     acc_dump, nullptr);
+    return hip_status(mq::launch_gemm(a, mq::GemmKind::Fused, static_cast<hipStream_t>(stream)));
+}
+
+int mq_gemm_w4a4_dense(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint16_t* sw,
+                       int64_t M, int64_t N, int64_t K, int group, void* y, int y_dtype,
+                       int32_t* acc_dump, void* stream) {
+    int rc = check_gemm(xq, sx, wq, sw, M, N, K, group, 64, mq::kBk, y, y_dtype);
+    if (rc) return rc;
+    if (M == 0) return MQ_OK;
+    const mq::GemmArgs a = make_args(xq, sx, wq, sw, nullptr, nullptr, nullptr, 0, M, N, K, 64, y, y_dtype,
+                                     acc_dump, nullptr);
+    return hip_status(mq::launch_gemm(a, mq::GemmKind::Dense, static_cast<hipStream_t>(stream)));
+}
+
+int mq_gemm_residual_separate(const uint8_t* xq, const float* sx, const uint8_t* wq,
+                              const uint16_t* sw, const int32_t* row_ptr, const int32_t* col_idx,
+                              const uint8_t* rq, int64_t nnz, int64_t M, int64_t N, int64_t K,
+                              int group, int bn, int bk, void* y, int y_dtype, float* ws,
+                              void* stream) {
+    int rc = check_gemm(xq, sx, wq, sw, M, N, K, group, bn, bk, y, y_dtype);
+    if (rc) return rc;
+    rc = check_csr(row_ptr, col_idx, rq, nnz, N, K, bn, bk);
+    if (rc) return rc;
+    if (M > 0 && !ws) return MQ_ERR_INVALID_ARG;
+    if (M == 0) return MQ_OK;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const mq::GemmArgs a = make_args(xq, sx, wq, sw, row_ptr, col_idx, rq, nnz, M, N, K, bn, y, y_dtype,
+                                     nullptr, ws);
+    hipError_t e = mq::launch_gemm(a, mq::GemmKind::DenseToWorkspace, st);
+    if (e != hipSuccess) return MQ_ERR_HIP;
+    return hip_status(mq::launch_residual_merge(a, st));
+}
+
+}  // extern "C"

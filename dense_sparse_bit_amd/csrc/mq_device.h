@@ -1,0 +1,111 @@
+// Device-side helpers shared by the MosaicQuant HIP kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mq {
+
+constexpr int kGroup = 128;   // weight group along K
+constexpr int kBk = 64;       // residual block width along K (two blocks per group)
+constexpr int kQmax = 7;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// binary16 bits <-> fp32 through the hardware conversions (round to nearest even;
+// fp16 denormals are kept by the default float mode).
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, b));
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float load_x(const void* x, bool bf16, int64_t i) {
+    return bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(x)[i])
+                : static_cast<const float*>(x)[i];
+}
+
+// Symmetric RTN code on scale s: 0 when s == 0, else clamp(rint(v / s), -7, 7).
+// fp32 division is the correctly rounded one (the library is built without
+// fast-math), rint is round-half-even.
+__device__ __forceinline__ int rtn_code(float v, float s) {
+    if (s == 0.0f) return 0;
+    float t = __builtin_rintf(v / s);
+    t = fminf(fmaxf(t, -7.0f), 7.0f);
+    return static_cast<int>(t);
+}
+
+// One element of the decomposition W ~ s*q + s_r*r for a group with fp16 scale s.
+struct Elem {
+    int q, r;
+    float e, ep;
+};
+__device__ __forceinline__ Elem quant_elem(float w, float s) {
+    Elem o;
+    o.q = rtn_code(w, s);
+    o.e = __builtin_fmaf(-s, static_cast<float>(o.q), w);
+    const float sr = s / 14.0f;
+    o.r = rtn_code(o.e, sr);
+    o.ep = __builtin_fmaf(-sr, static_cast<float>(o.r), o.e);
+    return o;
+}
+
+// ---- int4 -> int8 operand construction for the int8 MFMA ------------------
+// A 32-bit word holds 8 two's-complement nibbles (k0 in bits 0-3). Placing a
+// nibble in the high half of a byte gives the int8 value 16*v, so two masks
+// turn 8 nibbles into 8 int8 operands (k even in one dword, k odd in the other);
+// the same permutation of k is applied to both MFMA operands, which leaves the
+// dot product unchanged.
+__device__ __forceinline__ uint32_t nib16_even(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t nib16_odd(uint32_t w) { return w & 0xF0F0F0F0u; }
+
+// 16 bytes of nibbles (32 values) -> two MFMA operands of 16 int8 (values x16).
+__device__ __forceinline__ void unpack16(const uint4 w, v4i& op0, v4i& op1) {
+    op0 = v4i{(int)nib16_even(w.x), (int)nib16_odd(w.x), (int)nib16_even(w.y), (int)nib16_odd(w.y)};
+    op1 = v4i{(int)nib16_even(w.z), (int)nib16_odd(w.z), (int)nib16_even(w.w), (int)nib16_odd(w.w)};
+}
+
+// Combined operand 14*q + r per byte (plain int8, |value| <= 105), from the base
+// word wq and residual word wr. In offset form q' = q+8, r' = r+8 (nibble ^ 8)
+// every byte of 14*q' + r' + 8 stays in [23, 233], so whole-word integer
+// arithmetic produces each byte without carries; xor 0x80 then subtracts 128.
+__device__ __forceinline__ uint32_t comb_even(uint32_t qo, uint32_t ro) {
+    const uint32_t qe = qo & 0x0F0F0F0Fu, re = ro & 0x0F0F0F0Fu;
+    return (((qe << 4) - (qe << 1)) + re + 0x08080808u) ^ 0x80808080u;
+}
+__device__ __forceinline__ uint32_t comb_odd(uint32_t qo, uint32_t ro) {
+    const uint32_t q16 = qo & 0xF0F0F0F0u, rd = (ro >> 4) & 0x0F0F0F0Fu;
+    return ((q16 - (q16 >> 3)) + rd + 0x08080808u) ^ 0x80808080u;
+}
+__device__ __forceinline__ void unpack_comb(const uint4 wq, const uint4 wr, v4i& op0, v4i& op1) {
+    const uint32_t x = 0x88888888u;
+    const uint32_t q0 = wq.x ^ x, q1 = wq.y ^ x, q2 = wq.z ^ x, q3 = wq.w ^ x;
+    const uint32_t r0 = wr.x ^ x, r1 = wr.y ^ x, r2 = wr.z ^ x, r3 = wr.w ^ x;
+    op0 = v4i{(int)comb_even(q0, r0), (int)comb_odd(q0, r0), (int)comb_even(q1, r1), (int)comb_odd(q1, r1)};
+    op1 = v4i{(int)comb_even(q2, r2), (int)comb_odd(q2, r2), (int)comb_even(q3, r3), (int)comb_odd(q3, r3)};
+}
+
+__device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint8_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+}  // namespace mq

@@ -1,0 +1,39 @@
+// Internal launcher interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mq {
+
+struct GemmArgs {
+    const uint8_t* xq;
+    const float* sx;
+    const uint8_t* wq;
+    const uint16_t* sw;
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    const uint8_t* rq;
+    int nnz;
+    int M, N, K, bn;
+    void* y;
+    int y_bf16;
+    int32_t* acc_dump;
+    float* ws;
+};
+
+enum class GemmKind { Fused, Dense, DenseToWorkspace };
+
+hipError_t launch_hessian(const void* x, int bf16, int64_t M, int64_t K, float* h, hipStream_t st);
+hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, uint8_t* xq, float* sx,
+                            hipStream_t st);
+hipError_t launch_select(const float* w, const float* h, int64_t N, int64_t K, int bn,
+                         int64_t k_blocks, int32_t* row_ptr, int32_t* col_idx, double* delta,
+                         hipStream_t st);
+hipError_t launch_pack(const float* w, int64_t N, int64_t K, int bn, const int32_t* row_ptr,
+                       const int32_t* col_idx, int64_t nnz, uint8_t* wq, uint16_t* sw, uint8_t* rq,
+                       hipStream_t st);
+hipError_t launch_gemm(const GemmArgs& a, GemmKind kind, hipStream_t st);
+hipError_t launch_residual_merge(const GemmArgs& a, hipStream_t st);
+
+}  // namespace mq

@@ -1,0 +1,159 @@
+/*
+ * mq.h -- C ABI of the MI355X (gfx950) MosaicQuant library.
+ *
+ * The library computes the ZipperEngine path of MosaicQuant ("MosaicQuant:
+ * Inlier-Outlier Disaggregation for Unified 4-Bit LLM Quantization", technical
+ * summary on gist.science): a weight matrix W^ [N][K] (out x in) is decomposed as
+ * W^ ~ Q(W^) + R (Methodology 1), a dense 4-bit base plus a 4-bit residual kept
+ * only for the top-K (bn x bk) blocks ranked by a Hessian-guided Delta-score
+ * (Methodology 2), and Y = Xq Q(W^)^T + Xq R^T is computed by one fused kernel
+ * that walks the residual blocks inside the dense 4-bit GEMM (Methodology 3).
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is a DEVICE pointer (HBM), owned and allocated by the
+ *     caller; the library keeps no reference after the call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls are
+ *     asynchronous on it unless stated otherwise.
+ *   - Inputs are read-only. Outputs are fully overwritten. Inputs and outputs
+ *     must not overlap.
+ *   - int4 data are two's-complement nibbles, the low nibble of each byte holds
+ *     the even index, rows are contiguous (row-major).
+ *   - Packed buffers (xq, wq, rq) must be 16-byte aligned.
+ *   - Argument checks happen before any launch and return MQ_ERR_INVALID_ARG or
+ *     MQ_ERR_UNSUPPORTED with nothing written. A failed launch returns
+ *     MQ_ERR_HIP; faults inside a kernel surface at the caller's next
+ *     synchronisation of `stream`.
+ *   - Shapes the GPU path supports: K % 128 == 0, group == 128, bk == 64,
+ *     bn in {64, 128}, N % bn == 0. M may be any value >= 0 (M == 0 is a no-op).
+ *   - Inputs must be finite, and max|w| over a group must be below 7 * 65504
+ *     (the fp16 scale must be finite); otherwise results are unspecified.
+ */
+#ifndef MQ_H
+#define MQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MQ_OK = 0,
+    MQ_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned buffer, k_blocks > NB */
+    MQ_ERR_UNSUPPORTED = -2,  /* shape outside the supported set above */
+    MQ_ERR_HIP = -3           /* a HIP runtime call or launch failed */
+} mq_status;
+
+typedef enum { MQ_F32 = 0, MQ_BF16 = 1 } mq_dtype;
+
+/* Human-readable text for a status code (static storage). */
+const char* mq_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int mq_version(void);
+
+/*
+ * Diagonal-Hessian estimate of the input channels (Methodology 2: the
+ * "activation sensitivity" that weights the residual error in the Delta-score).
+ *   h[k] = fp32( (sum over m = 0..M-1, in ascending order, of (double)x[m][k]^2) / M )
+ * x: [M][K] fp32 or bf16 (x_dtype), h: fp32 [K]. M >= 1, K >= 1.
+ */
+int mq_hessian_diag(const void* x, int x_dtype, int64_t M, int64_t K, float* h, void* stream);
+
+/*
+ * Per-token symmetric int4 activation quantization (the W4A4 setting of the
+ * Experimental Results; "quantization" is the first stage of the ZipperEngine
+ * pipeline, Methodology 3).
+ *   sx[m] = fp32(max_k |x[m][k]| / 7)
+ *   xq[m][k] = sx[m] == 0 ? 0 : clamp(rint(x[m][k] / sx[m]), -7, 7)   (ties to even)
+ * x: [M][K] fp32 or bf16, xq: u8 [M][K/2], sx: fp32 [M]. K even.
+ */
+int mq_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* xq, float* sx,
+                    void* stream);
+
+/*
+ * Hessian-guided Delta-score of every (bn x bk) block and global top-k_blocks
+ * selection (Methodology 2 "Block-wise Residual Allocation").
+ * For element (n, k) of group g with fp16 base scale s (see mq_pack_weights):
+ *   q = base code, E = w - s*q, s_r = fp32(s / 14), r = clamp(rint(E / s_r), -7, 7),
+ *   E' = E - s_r*r (single rounding).
+ *   Delta_b = sum over rows n of b (ascending) of
+ *             [ sum over cols k of b (ascending) of (double)h[k] * (E^2 - E'^2) ]
+ * every fp64 operation rounded separately. Blocks are ranked by (Delta descending,
+ * id ascending), id = (n / bn) * (K / bk) + k / bk, and the first k_blocks are
+ * chosen. Output is CSR over block rows:
+ *   row_ptr: int32 [N/bn + 1], col_idx: int32 [k_blocks] (column-block index,
+ *   ascending within a row), delta: fp64 [NB] with NB = (N/bn)*(K/bk).
+ * w: fp32 [N][K], h: fp32 [K]. 0 <= k_blocks <= NB.
+ * Uses stream-ordered temporary device memory (hipMallocAsync) of NB bytes.
+ */
+int mq_select_blocks(const float* w, const float* h, int64_t N, int64_t K, int group, int bn,
+                     int bk, int64_t k_blocks, int32_t* row_ptr, int32_t* col_idx,
+                     double* delta, void* stream);
+
+/*
+ * Packs the dense 4-bit base for every group and the 4-bit residual payload for
+ * the chosen blocks (Methodology 1: W^ ~ Q(W^) + R, both parts 4-bit).
+ *   sw[n][g] = fp16_rne( fp32(max_{k in g} |w[n][k]|) / 7 )      (fp16 bits)
+ *   wq[n][k] = s == 0 ? 0 : clamp(rint(w / s), -7, 7)  with s = fp32(sw[n][g])
+ *   rq[p][i][c] = residual code r (see mq_select_blocks) of row (row_block*bn + i),
+ *                 column (col_idx[p]*bk + c) for CSR entry p, in CSR order.
+ * w: fp32 [N][K]; row_ptr/col_idx as produced by mq_select_blocks (nnz entries);
+ * wq: u8 [N][K/2], sw: u16 [N][K/group], rq: u8 [nnz][bn][bk/2] (may be NULL if nnz == 0).
+ * Entries with a column-block index outside [0, K/bk) are skipped.
+ */
+int mq_pack_weights(const float* w, int64_t N, int64_t K, int group, int bn, int bk,
+                    const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                    uint8_t* wq, uint16_t* sw, uint8_t* rq, void* stream);
+
+/*
+ * The fused ZipperEngine GEMM (Methodology 3): one kernel streams the packed base
+ * and, inside the same K-loop, the residual blocks listed for its rows; both
+ * products accumulate into the same exact int32 partial sums per 128-group, which
+ * are dequantized and summed in fp32:
+ *   T[m][n][g] = 14 * P + Pr,  P = sum_{k in g} xq*q,  Pr = sum over chosen blocks in g of xq*r
+ *   y[m][n]    = sx[m] * sum_g ( groups with a chosen block in this row: s_r * T,
+ *                                otherwise s * P )            (fp32; s_r = fp32(s/14))
+ * which equals sx * sum_g (s*P + s_r*Pr) up to fp32 rounding.
+ * xq: u8 [M][K/2], sx: fp32 [M], wq: u8 [N][K/2], sw: u16 [N][K/group],
+ * row_ptr: int32 [N/bn+1], col_idx: int32 [nnz], rq: u8 [nnz][bn][bk/2] (NULL if nnz == 0),
+ * y: [M][N] fp32 or bf16 (y_dtype, bf16 rounded to nearest even).
+ * acc_dump: NULL, or int32 [M][N][K/group] receiving T (a debug build of the same
+ * kernel; production calls pass NULL). Indices outside the CSR ranges are ignored,
+ * so a malformed list gives wrong values, never an out-of-bounds access.
+ */
+int mq_gemm_w4a4_residual(const uint8_t* xq, const float* sx, const uint8_t* wq,
+                          const uint16_t* sw, const int32_t* row_ptr, const int32_t* col_idx,
+                          const uint8_t* rq, int64_t nnz, int64_t M, int64_t N, int64_t K,
+                          int group, int bn, int bk, void* y, int y_dtype, int32_t* acc_dump,
+                          void* stream);
+
+/*
+ * Dense-only 4-bit GEMM: the same kernel with the residual path compiled out
+ * (the "dense 4-bit GEMM kernel" the residual is fused into, Methodology 3).
+ * y = sx * sum_g s * P. With nnz == 0 the fused call gives the same bits.
+ * acc_dump (optional) receives T = 14 * P.
+ */
+int mq_gemm_w4a4_dense(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint16_t* sw,
+                       int64_t M, int64_t N, int64_t K, int group, void* y, int y_dtype,
+                       int32_t* acc_dump, void* stream);
+
+/*
+ * The separate-kernel alternative that Methodology 3 argues against: the dense
+ * kernel writes fp32 partial outputs to `ws` (fp32 [M][N], caller-allocated),
+ * then a second kernel re-reads the activations, computes the residual product
+ * block by block, merges it into the partial outputs and writes y.
+ * y = sx * sum_g (s*P + s_r*Pr) up to fp32 rounding. Same arguments as the fused
+ * call plus ws.
+ */
+int mq_gemm_residual_separate(const uint8_t* xq, const float* sx, const uint8_t* wq,
+                              const uint16_t* sw, const int32_t* row_ptr, const int32_t* col_idx,
+                              const uint8_t* rq, int64_t nnz, int64_t M, int64_t N, int64_t K,
+                              int group, int bn, int bk, void* y, int y_dtype, float* ws,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQ_H */

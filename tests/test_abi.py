@@ -1,0 +1,114 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol that
+include/mq.h declares, and rejects bad arguments before any launch (so these
+run without a GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mq.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(mq_[a-z0-9_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def mq():
+    from dense_sparse_bit_amd import _build
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    import dense_sparse_bit_amd
+    return dense_sparse_bit_amd
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for fn in ["mq_quantize_act", "mq_pack_weights", "mq_select_blocks", "mq_gemm_w4a4_residual",
+               "mq_hessian_diag", "mq_gemm_w4a4_dense", "mq_gemm_residual_separate",
+               "mq_status_string", "mq_version"]:
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(mq):
+    lib = C.CDLL(mq.LIB_PATH)
+    for fn in _declared():
+        assert hasattr(lib, fn), fn
+    assert set(_declared()) == set(mq.EXPORTS)
+    assert mq.version() == 10000
+    for s in (0, -1, -2, -3):
+        assert mq.status_string(s)
+
+
+FAKE = 0x10000   # never dereferenced: every call below fails its checks first
+
+
+@pytest.fixture(scope="module")
+def lib_nogpu(mq):
+    """The raw library, only where no GPU is visible: a fake-pointer call that
+    slipped past a check would launch, which must never happen on a real GPU."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only argument checks run where no GPU is visible")
+    return mq.lib()
+
+
+def _gemm(lib, **kw):
+    a = dict(xq=FAKE, sx=FAKE, wq=FAKE, sw=FAKE, row_ptr=FAKE, col_idx=FAKE, rq=FAKE, nnz=10, M=4,
+             N=512, K=512, group=128, bn=64, bk=64, y=FAKE, y_dtype=1, dump=None, stream=None)
+    a.update(kw)
+    return lib.mq_gemm_w4a4_residual(a["xq"], a["sx"], a["wq"], a["sw"], a["row_ptr"], a["col_idx"],
+                                     a["rq"], a["nnz"], a["M"], a["N"], a["K"], a["group"], a["bn"],
+                                     a["bk"], a["y"], a["y_dtype"], a["dump"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=500), -2), (dict(K=192), -2), (dict(N=500), -2), (dict(group=64), -2),
+    (dict(bk=32), -2), (dict(bn=32), -2), (dict(bn=128, N=64 * 3), -2), (dict(N=0), -1),
+    (dict(M=-1), -1), (dict(y_dtype=7), -1), (dict(xq=None), -1), (dict(wq=None), -1),
+    (dict(sw=None), -1), (dict(row_ptr=None), -1), (dict(col_idx=None), -1), (dict(rq=None), -1),
+    (dict(xq=FAKE + 8), -1), (dict(rq=FAKE + 4), -1), (dict(nnz=-1), -1), (dict(nnz=65), -1),
+])
+def test_gemm_rejects_bad_arguments(lib_nogpu, kw, status):
+    assert _gemm(lib_nogpu, **kw) == status
+
+
+def test_zero_tokens_is_a_no_op(lib_nogpu):
+    # M == 0 returns before any launch, even with no activation buffers
+    assert _gemm(lib_nogpu, M=0, xq=None, sx=None, y=None) == 0
+
+
+def test_preparation_calls_reject_bad_arguments(lib_nogpu):
+    lib = lib_nogpu
+    assert lib.mq_quantize_act(FAKE, 1, 4, 511, FAKE, FAKE, None) == -1
+    assert lib.mq_quantize_act(FAKE, 3, 4, 512, FAKE, FAKE, None) == -1
+    assert lib.mq_quantize_act(None, 1, 0, 512, None, None, None) == 0
+    assert lib.mq_hessian_diag(FAKE, 1, 0, 512, FAKE, None) == -1
+    assert lib.mq_hessian_diag(None, 1, 4, 512, FAKE, None) == -1
+    nb = (512 // 64) * (512 // 64)
+    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, nb + 1, FAKE, FAKE, FAKE, None) == -1
+    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, -1, FAKE, FAKE, FAKE, None) == -1
+    assert lib.mq_select_blocks(FAKE, FAKE, 512, 500, 128, 64, 64, 3, FAKE, FAKE, FAKE, None) == -2
+    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, 3, FAKE, FAKE, None, None) == -1
+    assert lib.mq_pack_weights(FAKE, 512, 512, 128, 64, 64, None, FAKE, 3, FAKE, FAKE, FAKE, None) == -1
+    assert lib.mq_pack_weights(FAKE + 4, 512, 512, 128, 64, 64, FAKE, FAKE, 3, FAKE, FAKE, FAKE, None) == -1
+    assert lib.mq_gemm_w4a4_dense(FAKE, FAKE, FAKE, FAKE, 4, 512, 320, 128, FAKE, 0, None, None) == -2
+    assert lib.mq_gemm_residual_separate(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 4, 512, 512,
+                                         128, 64, 64, FAKE, 0, None, None) == -1
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    """The package has no fallback: with the library absent, import raises."""
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "dense_sparse_bit_amd")
+    dst = tmp_path / "dense_sparse_bit_amd"
+    dst.mkdir()
+    (dst / "__init__.py").write_text(open(os.path.join(pkg, "__init__.py")).read())
+    r = subprocess.run([sys.executable, "-c", "import dense_sparse_bit_amd"], cwd=str(tmp_path),
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0 and "libmq.so is missing" in r.stderr

@@ -1,0 +1,241 @@
+"""GPU parity: every step of the HIP path against the CPU oracle, through the C ABI.
+
+Bit-exact: h, delta, row_ptr/col_idx, wq/sw/rq, xq/sx and the int32 group
+accumulators T = 14*P + Pr. Within tolerance: y (max relative error, floor
+0.1*rms of the row: fp32 output <= 1e-3, bf16 output <= 1e-2). The dense-only
+kernel must equal the fused kernel with an empty residual bit for bit.
+
+Inputs are the seeded synthetic workloads of synth.py at their full sizes; for
+the 2048-token prefill the oracle's integer sums and outputs are compared on a
+sample of 80 token rows (rows 0-63, which hold the BOS-like row, plus 16 drawn
+rows), every other quantity in full.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from tests.nibbles import f16_bits_to_f32, rel_err
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = {"f32": 1e-3, "bf16": 1e-2}
+_ORACLE = {}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def mq():
+    import torch
+    assert torch.cuda.is_available(), "GPU parity tests need a visible MI355X"
+    import dense_sparse_bit_amd
+    return dense_sparse_bit_amd
+
+
+def _inputs(cfg_or_name):
+    key = cfg_or_name if isinstance(cfg_or_name, str) else cfg_or_name
+    if ("inp", key) not in _ORACLE:
+        _ORACLE[("inp", key)] = synth.make_inputs(cfg_or_name)
+    return _ORACLE[("inp", key)]
+
+
+def _oracle_prep(orc, inp):
+    """Oracle steps that do not depend on the budget."""
+    key = ("prep", inp.cfg)
+    if key not in _ORACLE:
+        cfg = inp.cfg
+        h = orc.hessian_diag(inp.x_raw())
+        delta = orc.delta_scores(inp.W, h, cfg.group, cfg.bn, cfg.bk)
+        xq, sx = orc.quantize_act(inp.x_raw())
+        _ORACLE[key] = dict(h=h, delta=delta, xq=xq, sx=sx)
+    return _ORACLE[key]
+
+
+def _oracle_budget(orc, inp, k_blocks, rows=None):
+    key = ("budget", inp.cfg, k_blocks, None if rows is None else tuple(rows))
+    if key not in _ORACLE:
+        cfg = inp.cfg
+        pre = _oracle_prep(orc, inp)
+        rp, ci, sel = orc.select_topk(pre["delta"], cfg.N // cfg.bn, cfg.K // cfg.bk, k_blocks)
+        wq, sw, rq = orc.pack_weights(inp.W, rp, ci, cfg.group, cfg.bn, cfg.bk)
+        xq, sx = pre["xq"], pre["sx"]
+        if rows is not None:
+            xq, sx = xq[rows], sx[rows]
+        P, Pr = orc.accumulators(xq, wq, rp, ci, rq, cfg.K, cfg.group, cfg.bn, cfg.bk)
+        y = orc.output(sx, sw, P, Pr)
+        T = 14 * P.astype(np.int64) + Pr
+        _ORACLE[key] = dict(row_ptr=rp, col_idx=ci, wq=wq, sw=sw, rq=rq, T=T, P=P, y=y)
+    return _ORACLE[key]
+
+
+def _to_dev(a, dtype=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def _x_dev(inp):
+    import torch
+    if inp.X_bits is not None:
+        return _to_dev(inp.X_bits.view(np.int16), torch.bfloat16)
+    return _to_dev(inp.X)
+
+
+def _np(t):
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.float().numpy()
+    return t.numpy()
+
+
+def _run_gpu(mq, inp, k_blocks, out_dtype):
+    import torch
+    cfg = inp.cfg
+    x = _x_dev(inp)
+    w = _to_dev(inp.W)
+    h = mq.hessian_diag(x)
+    rp, ci, delta = mq.select_blocks(w, h, k_blocks, bn=cfg.bn)
+    wq, sw, rq = mq.pack_weights(w, rp, ci, bn=cfg.bn)
+    xq, sx = mq.quantize_act(x)
+    dump = torch.empty((cfg.M, cfg.N, cfg.K // 128), dtype=torch.int32, device="cuda")
+    y = mq.gemm_w4a4_residual(xq, sx, wq, sw, rp, ci, rq, cfg.K, bn=cfg.bn, out_dtype=out_dtype,
+                              acc_dump=dump)
+    torch.cuda.synchronize()
+    return dict(h=h, row_ptr=rp, col_idx=ci, delta=delta, wq=wq, sw=sw, rq=rq, xq=xq, sx=sx, y=y,
+                dump=dump, w=w, x=x)
+
+
+def _check(mq, orc, inp, k_blocks, out_dtype_name="bf16", rows=None, check_variants=True):
+    import torch
+    cfg = inp.cfg
+    out_dtype = torch.bfloat16 if out_dtype_name == "bf16" else torch.float32
+    say(f"[parity] {cfg.name} M={cfg.M} K={cfg.K} N={cfg.N} bn={cfg.bn} k_blocks={k_blocks} "
+        f"y={out_dtype_name} W={synth.sha256(inp.W)} X={synth.sha256(inp.X)}")
+    pre = _oracle_prep(orc, inp)
+    ref = _oracle_budget(orc, inp, k_blocks, rows)
+    g = _run_gpu(mq, inp, k_blocks, out_dtype)
+    np.testing.assert_array_equal(_np(g["h"]), pre["h"])
+    np.testing.assert_array_equal(_np(g["delta"]), pre["delta"])
+    np.testing.assert_array_equal(_np(g["row_ptr"]), ref["row_ptr"])
+    np.testing.assert_array_equal(_np(g["col_idx"]), ref["col_idx"])
+    np.testing.assert_array_equal(_np(g["wq"]), ref["wq"])
+    np.testing.assert_array_equal(_np(g["sw"]).view(np.uint16), ref["sw"])
+    np.testing.assert_array_equal(_np(g["rq"]), ref["rq"])
+    np.testing.assert_array_equal(_np(g["xq"]), pre["xq"])
+    np.testing.assert_array_equal(_np(g["sx"]), pre["sx"])
+    sel = slice(None) if rows is None else rows
+    dump = g["dump"][sel] if rows is None else g["dump"][torch.as_tensor(rows, device="cuda")]
+    np.testing.assert_array_equal(_np(dump).astype(np.int64), ref["T"])
+    y = _np(g["y"])[sel]
+    err = rel_err(y, ref["y"])
+    say(f"[parity] {cfg.name} y max rel err {err:.3e}")
+    assert err <= Y_TOL[out_dtype_name]
+    if check_variants:
+        # dense-only kernel: T = 14 P, and y equals the fused kernel with no residual
+        ddump = torch.empty_like(g["dump"])
+        yd = mq.gemm_w4a4_dense(g["xq"], g["sx"], g["wq"], g["sw"], cfg.K, out_dtype=out_dtype,
+                                acc_dump=ddump)
+        empty = torch.zeros(cfg.N // cfg.bn + 1, dtype=torch.int32, device="cuda")
+        none = torch.empty(0, dtype=torch.int32, device="cuda")
+        y0 = mq.gemm_w4a4_residual(g["xq"], g["sx"], g["wq"], g["sw"], empty, none, none, cfg.K,
+                                   bn=cfg.bn, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(yd.view(torch.int16) if out_dtype == torch.bfloat16 else yd.view(torch.int32),
+                           y0.view(torch.int16) if out_dtype == torch.bfloat16 else y0.view(torch.int32))
+        dd = ddump if rows is None else ddump[torch.as_tensor(rows, device="cuda")]
+        np.testing.assert_array_equal(_np(dd).astype(np.int64), 14 * ref["P"].astype(np.int64))
+        # the separate-kernel alternative computes the same y within tolerance
+        ys = mq.gemm_residual_separate(g["xq"], g["sx"], g["wq"], g["sw"], g["row_ptr"], g["col_idx"],
+                                       g["rq"], cfg.K, bn=cfg.bn, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        err_s = rel_err(_np(ys)[sel], ref["y"])
+        say(f"[parity] {cfg.name} separate-kernel y max rel err {err_s:.3e}")
+        assert err_s <= Y_TOL[out_dtype_name]
+    del g
+    torch.cuda.empty_cache()
+
+
+# --------------------------------------------------------------------------- the workloads
+@pytest.mark.parametrize("name", ["tiny", "llama3_8b_qo", "llama3_8b_up_m4", "llama3_8b_up_m32",
+                                  "llama3_8b_down_m4", "llama3_8b_down_m32", "qwen3_32b_up",
+                                  "qwen3_32b_down"])
+def test_decode_workload(mq, orc, name):
+    inp = _inputs(name)
+    cfg = inp.cfg
+    out = "f32" if name == "tiny" else "bf16"
+    _check(mq, orc, inp, cfg.k_blocks(cfg.default_budget), out)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_up_m32", "llama3_8b_down_m4"])
+@pytest.mark.parametrize("pct", [0, 5, 20])
+def test_budget_sweep(mq, orc, name, pct):
+    inp = _inputs(name)
+    _check(mq, orc, inp, inp.cfg.k_blocks(pct), "bf16", check_variants=(pct == 0))
+
+
+@pytest.mark.parametrize("pct", [10, 0])
+def test_prefill_workload_sampled_rows(mq, orc, pct):
+    inp = _inputs("qwen3_14b_prefill")
+    rng = np.random.default_rng(123)
+    rows = np.concatenate([np.arange(64), np.sort(rng.choice(np.arange(64, inp.cfg.M), 16, replace=False))])
+    _check(mq, orc, inp, inp.cfg.k_blocks(pct), "bf16", rows=rows, check_variants=(pct == 10))
+
+
+# --------------------------------------------------------------------------- edge cases
+EDGE = [
+    # several tiles of the tiled kernel with ragged M and N tails, 64-row blocks
+    synth.custom_config("tiled_ragged", M=300, K=1024, N=320, bn=64),
+    synth.custom_config("tiled_bn128", M=100, K=768, N=384, bn=128, x_bos_scale=100.0),
+    # skinny kernel edges: one token, 17 and 31 tokens, 128-row blocks
+    synth.custom_config("one_token", M=1, K=512, N=256, bn=64, x_bf16=False),
+    synth.custom_config("m17", M=17, K=640, N=192, bn=64),
+    synth.custom_config("m31_bn128", M=31, K=1280, N=256, bn=128),
+    synth.custom_config("m33_tiled_small", M=33, K=256, N=128, bn=64, x_dist="t3"),
+    # long K: one wavefront per 4 groups up to 16, plus uneven splits
+    synth.custom_config("long_k", M=8, K=128 * 75, N=128, bn=64),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=[c.name for c in EDGE])
+@pytest.mark.parametrize("pct", [0, 10, 100])
+def test_edge_shapes(mq, orc, cfg, pct):
+    inp = _inputs(cfg)
+    _check(mq, orc, inp, cfg.k_blocks(pct), "f32" if pct == 10 else "bf16",
+           check_variants=(pct != 100))
+
+
+def test_degenerate_rows_and_groups(mq, orc):
+    """All-zero token (sx = 0), all-zero weight groups (s = 0), a group whose fp16
+    scale is subnormal, a one-hot group, and every block chosen."""
+    cfg = synth.custom_config("degenerate", M=20, K=512, N=128, bn=64)
+    inp = synth.make_inputs(cfg)
+    inp.X[5] = 0.0
+    inp.X_bits[5] = 0
+    inp.W[3, 0:128] = 0.0
+    inp.W[7, 256:384] = np.float32(2.0 ** -20) * np.float32([7, -3, 1, 0.5] * 32)
+    inp.W[9, 128:256] = 0.0
+    inp.W[9, 200] = -0.75
+    inp.W[70:128, 384:512] = 0.0     # whole zero blocks
+    _check(mq, orc, inp, cfg.k_blocks(100), "f32")
+    _check(mq, orc, inp, 7, "bf16")
+
+
+def test_zero_tokens_no_op(mq):
+    import torch
+    xq = torch.empty((0, 256), dtype=torch.uint8, device="cuda")
+    sx = torch.empty(0, dtype=torch.float32, device="cuda")
+    wq = torch.zeros((128, 256), dtype=torch.uint8, device="cuda")
+    sw = torch.zeros((128, 4), dtype=torch.int16, device="cuda")
+    rp = torch.zeros(3, dtype=torch.int32, device="cuda")
+    none = torch.empty(0, dtype=torch.int32, device="cuda")
+    y = mq.gemm_w4a4_residual(xq, sx, wq, sw, rp, none, none, 512, bn=64)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 128)
