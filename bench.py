@@ -1,0 +1,372 @@
+"""Benchmark of the MosaicQuant path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole path over one batch of synthetic input, every
+step on the GPU: the diagonal-Hessian estimate of the batch, Delta-score top-K
+block selection, packing of the 4-bit base and residual, per-token activation
+quantization and the fused W4A4 + sparse-residual GEMM. Inputs are resident in
+HBM before the timed region; consecutive steps read different copies of them
+(more than 600 MB in total) so the 256 MB Infinity Cache cannot serve them.
+
+Printed on stdout: one JSON line. `value` is the step's algorithmic HBM bytes
+per second; `roofline` is the kernel that takes most of the step, timed with
+HIP events on the launch stream; `gemm` is the fused kernel alone (the metric's
+TOPS and GB/s), timed over rotated packed-weight copies, beside the dense-only
+kernel and the separate-kernel alternative; `cpu_baseline` is the CPU oracle on
+the host, one core, on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "fused W4A4+10% residual GEMM: TOPS & HBM GB/s (% roofline); overhead vs dense"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA
+ROTATE_BYTES = 640 << 20        # > 2 x (256 MB Infinity Cache + 8 x 4 MB L2)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------- algorithmic work
+def gemm_bytes(cfg, nnz, residual=True, y_bytes=2):
+    M, N, K, G = cfg.M, cfg.N, cfg.K, cfg.K // cfg.group
+    b = N * K // 2 + N * G * 2 + M * K // 2 + M * 4 + M * N * y_bytes
+    if residual:
+        b += nnz * cfg.bn * cfg.bk // 2 + nnz * 4 + (N // cfg.bn + 1) * 4
+    return b
+
+
+def gemm_ops(cfg, nnz, residual=True):
+    return 2 * cfg.M * (cfg.N * cfg.K + (nnz * cfg.bn * cfg.bk if residual else 0))
+
+
+def step_bytes(cfg, nnz, x_bytes):
+    """Bytes each call of the step must move at minimum (read inputs once, write outputs once)."""
+    M, N, K, G = cfg.M, cfg.N, cfg.K, cfg.K // cfg.group
+    nb = (N // cfg.bn) * (K // cfg.bk)
+    csr = (N // cfg.bn + 1) * 4 + nnz * 4
+    return {
+        "hessian_diag": M * K * x_bytes + K * 4,
+        "select_blocks": N * K * 4 + K * 4 + nb * 8 + csr,
+        "pack_weights": N * K * 4 + csr + N * K // 2 + N * G * 2 + nnz * cfg.bn * cfg.bk // 2,
+        "quantize_act": M * K * x_bytes + M * K // 2 + M * 4,
+        "gemm_w4a4_residual": gemm_bytes(cfg, nnz),
+    }
+
+
+# --------------------------------------------------------------------------- GPU legs
+def bench_step(mq, torch, cfg, inp, k_blocks, steps, warmup):
+    dev = torch.device("cuda:0")
+    x_bytes = 2 if inp.X_bits is not None else 4
+    per_copy = cfg.N * cfg.K * 4 + cfg.M * cfg.K * x_bytes
+    copies = max(2, min(64, -(-ROTATE_BYTES // per_copy)))
+    if inp.X_bits is not None:
+        x0 = torch.from_numpy(inp.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        x0 = torch.from_numpy(inp.X).to(dev)
+    w0 = torch.from_numpy(inp.W).to(dev)
+    xs = [x0.clone() for _ in range(copies)]
+    ws = [w0.clone() for _ in range(copies)]
+    del x0, w0
+    N, K, M, bn = cfg.N, cfg.K, cfg.M, cfg.bn
+    nb = (N // bn) * (K // cfg.bk)
+    h = torch.empty(K, dtype=torch.float32, device=dev)
+    sel_out = (torch.empty(N // bn + 1, dtype=torch.int32, device=dev),
+               torch.empty(max(k_blocks, 1), dtype=torch.int32, device=dev),
+               torch.empty(nb, dtype=torch.float64, device=dev))
+    pack_out = (torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
+                torch.empty((N, K // 128), dtype=torch.int16, device=dev),
+                torch.empty((max(k_blocks, 1), bn, 32), dtype=torch.uint8, device=dev))
+    xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    sx = torch.empty(M, dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    names = ["hessian_diag", "select_blocks", "pack_weights", "quantize_act", "gemm_w4a4_residual"]
+    log(f"[bench] step workload {cfg.name}: M={M} K={K} N={N} bn={bn} k_blocks={k_blocks}, "
+        f"{copies} input copies ({copies * per_copy / 2**20:.0f} MiB)")
+
+    def one_step(i, ev=None):
+        x, w = xs[i % copies], ws[i % copies]
+        if ev is not None:
+            ev[0].record()
+        mq.hessian_diag(x, out=h)
+        if ev is not None:
+            ev[1].record()
+        rp, ci, _ = mq.select_blocks(w, h, k_blocks, bn=bn, out=sel_out)
+        if ev is not None:
+            ev[2].record()
+        wq, sw, rq = mq.pack_weights(w, rp, ci, bn=bn, out=pack_out)
+        if ev is not None:
+            ev[3].record()
+        mq.quantize_act(x, xq=xq, sx=sx)
+        if ev is not None:
+            ev[4].record()
+        mq.gemm_w4a4_residual(xq, sx, wq, sw, rp, ci, rq, K, bn=bn, y=y)
+        if ev is not None:
+            ev[5].record()
+
+    for i in range(warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one_step(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: [] for n in names}
+    for ev in evs:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)   # us
+    gpu_ms = sum(evs[i][0].elapsed_time(evs[i][5]) for i in range(steps)) / steps
+    del xs, ws
+    torch.cuda.empty_cache()
+    return dict(wall_ms=wall * 1e3 / steps, gpu_ms=gpu_ms,
+                us={n: float(np.mean(v)) for n, v in per.items()},
+                us_median={n: float(np.median(v)) for n, v in per.items()})
+
+
+def bench_gemm(mq, torch, cfg, inp, k_blocks, calls):
+    """Fused, dense-only and separate-kernel GEMM over rotated packed-weight copies."""
+    dev = torch.device("cuda:0")
+    if inp.X_bits is not None:
+        x = torch.from_numpy(inp.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        x = torch.from_numpy(inp.X).to(dev)
+    w = torch.from_numpy(inp.W).to(dev)
+    g = mq.forward_layer(x, w, k_blocks, bn=cfg.bn)
+    del w
+    packed = gemm_bytes(cfg, k_blocks) - cfg.M * (cfg.K // 2 + 4 + cfg.N * 2)
+    copies = max(2, min(256, -(-ROTATE_BYTES // packed)))
+    sets = [(g["wq"].clone(), g["sw"].clone(), g["rq"].clone(), g["row_ptr"].clone(),
+             g["col_idx"].clone()) for _ in range(copies)]
+    xq, sx, K, bn = g["xq"], g["sx"], cfg.K, cfg.bn
+    y = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device=dev)
+    wsb = torch.empty((cfg.M, cfg.N), dtype=torch.float32, device=dev)
+    log(f"[bench] gemm legs: {copies} packed-weight copies ({copies * packed / 2**20:.0f} MiB), "
+        f"{calls} calls each")
+
+    def fused(i):
+        wq, sw, rq, rp, ci = sets[i % copies]
+        mq.gemm_w4a4_residual(xq, sx, wq, sw, rp, ci, rq, K, bn=bn, y=y)
+
+    def dense(i):
+        wq, sw, *_ = sets[i % copies]
+        mq.gemm_w4a4_dense(xq, sx, wq, sw, K, y=y)
+
+    def separate(i):
+        wq, sw, rq, rp, ci = sets[i % copies]
+        mq.gemm_residual_separate(xq, sx, wq, sw, rp, ci, rq, K, bn=bn, y=y, ws=wsb)
+
+    out = {}
+    for name, fn in (("dense", dense), ("fused", fused), ("separate", separate)):
+        # eager result of the last call, to check the graph replays against
+        fn(calls - 1)
+        torch.cuda.synchronize()
+        y_eager = y.clone()
+        # capture `calls` back-to-back launches in one HIP graph, so the timing is
+        # the kernels' and not the Python launch path's
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(3):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(calls):
+                fn(i)
+        reps = []
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
+                raise RuntimeError(f"graph replay of the {name} GEMM differs from the eager call")
+            reps.append(e0.elapsed_time(e1) * 1e3 / calls)
+        reps = reps[1:]
+        out[name] = float(np.median(reps))
+        log(f"[bench] gemm {name}: {out[name]:.3f} us/call (graph replays {[round(r, 3) for r in reps]})")
+        del graph
+    return out
+
+
+# --------------------------------------------------------------------------- calibration
+def calibrate(torch, sizes_mb=(9.65, 64.0, 512.0), calls=50):
+    """Achievable HBM rate of a plain device copy (torch's copy kernel) at the sizes
+    this path moves, over rotating slices of a 1 GiB source so the Infinity Cache
+    cannot serve the reads; and the duration of a one-element fill (launch floor)."""
+    dev = torch.device("cuda:0")
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    out = {}
+    for mb in sizes_mb:
+        n = int(mb * 1e6) // 256 * 256
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        slices = max(1, (1 << 30) // n)
+        for i in range(5):
+            dst.copy_(src[(i % slices) * n:(i % slices) * n + n])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(calls):
+            j = i % slices
+            dst.copy_(src[j * n:j * n + n])
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / calls
+        out[f"copy_{mb:g}MB"] = {"us": round(us, 3), "GB/s(read+write)": round(2 * n / us / 1e3, 1)}
+        log(f"[bench] calib copy {mb:g} MB: {us:.2f} us/call, {2 * n / us / 1e3:.0f} GB/s read+write")
+        del dst
+    tiny = torch.empty(1, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(200):
+        tiny.fill_(1.0)
+    e1.record()
+    torch.cuda.synchronize()
+    out["fill_1_element_us"] = round(e0.elapsed_time(e1) * 1e3 / 200, 3)
+    del src
+    torch.cuda.empty_cache()
+    return out
+
+
+# --------------------------------------------------------------------------- CPU oracle leg
+def cpu_baseline(cfg, inp, k_blocks, seconds, step_total_bytes):
+    import oracle
+    orc = oracle.Oracle()
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        orc.forward(inp.x_raw(), inp.W, k_blocks, cfg.group, cfg.bn, cfg.bk)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or runs >= 50:
+            break
+    per = el / runs
+    return {"value": step_total_bytes / per / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{runs} full passes of the whole path on this workload (all steps, all "
+                      f"{cfg.M} tokens), single-threaded C, {per * 1e3:.0f} ms per pass",
+            "s_per_step": per}
+
+
+# --------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=synth.BENCH_CONFIG, choices=sorted(synth.CONFIGS))
+    ap.add_argument("--budget", type=int, default=None, help="residual budget in percent")
+    ap.add_argument("--gemm-calls", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-calib", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU leg in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dense_sparse_bit_amd as mq
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    cfg = synth.CONFIGS[args.workload]
+    pct = cfg.default_budget if args.budget is None else args.budget
+    k_blocks = cfg.k_blocks(pct)
+    inp = synth.make_inputs(cfg)
+    x_bytes = 2 if inp.X_bits is not None else 4
+    sb = step_bytes(cfg, k_blocks, x_bytes)
+    total_bytes = sum(sb.values())
+
+    st = bench_step(mq, torch, cfg, inp, k_blocks, args.steps, args.warmup)
+    kernels = {}
+    for n, us in st["us"].items():
+        gbs = sb[n] / us / 1e3
+        kernels[n] = {"us": round(us, 3), "bytes": sb[n], "GB/s": round(gbs, 1),
+                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    dom = max(st["us"], key=st["us"].get)
+    value = total_bytes / (st["gpu_ms"] * 1e-3) / 1e9
+
+    gemm = None
+    if not args.no_gemm:
+        t = bench_gemm(mq, torch, cfg, inp, k_blocks, args.gemm_calls)
+        fb, db = gemm_bytes(cfg, k_blocks), gemm_bytes(cfg, k_blocks, residual=False)
+        fo, do = gemm_ops(cfg, k_blocks), gemm_ops(cfg, k_blocks, residual=False)
+        leg = lambda us, b, o: {"us": round(us, 3), "GB/s": round(b / us / 1e3, 1),
+                                "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                                "TOPS": round(o / us / 1e6, 3),
+                                "int8_frac": round(o / us / 1e6 / INT8_PEAK_TOPS, 5), "bytes": b,
+                                "ops": o}
+        gemm = {"fused": leg(t["fused"], fb, fo), "dense": leg(t["dense"], db, do),
+                "separate": leg(t["separate"], fb, fo),
+                "overhead_vs_dense": round(t["fused"] / t["dense"] - 1, 4),
+                "separate_overhead_vs_dense": round(t["separate"] / t["dense"] - 1, 4),
+                "residual_bytes_vs_base": round((fb - db) / (cfg.N * cfg.K // 2 + cfg.N * cfg.K // 64), 4),
+                "timing": "median of 5 HIP-graph replays of %d back-to-back calls over rotated "
+                          "packed-weight copies, HIP events around each replay" % args.gemm_calls}
+
+    calib = None if args.no_calib else calibrate(torch)
+
+    cpu = None
+    if not args.no_cpu:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(cfg, inp, k_blocks, args.cpu_seconds, total_bytes)
+
+    dom_b = sb[dom]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(st["gpu_ms"], 5),
+        "wall_ms_per_step": round(st["wall_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic, seeded (synth.py): random weights and activations with the shapes and "
+                "outlier structure of the workload",
+        "config": {"workload": f"{cfg.name}: M={cfg.M} K={cfg.K} N={cfg.N}, residual budget {pct}% "
+                               f"of {cfg.bn}x{cfg.bk} blocks ({k_blocks}/{(cfg.N // cfg.bn) * (cfg.K // cfg.bk)}), "
+                               f"int4 weights group 128, per-token int4 activations",
+                   "M": cfg.M, "K": cfg.K, "N": cfg.N, "bn": cfg.bn, "bk": cfg.bk,
+                   "budget_pct": pct, "k_blocks": k_blocks,
+                   "step": "hessian_diag -> select_blocks -> pack_weights -> quantize_act -> "
+                           "gemm_w4a4_residual"},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_b / st["us"][dom] / 1e3, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_b / st["us"][dom] / 1e3 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": dom_b, "us_per_launch": round(st["us"][dom], 3)},
+        "cpu_baseline": None if cpu is None else {k: (round(v, 4) if isinstance(v, float) else v)
+                                                  for k, v in cpu.items() if k != "s_per_step"},
+        "step_kernels": kernels,
+        "gemm": gemm,
+        "calib": calib,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,8 +21,8 @@ int check_layer(int64_t N, int64_t K, int group, int bn, int bk) {
     if (N <= 0 || K <= 0) return MQ_ERR_INVALID_ARG;
     if (group != mq::kGroup || bk != mq::kBk || (bn != 64 && bn != 128)) return MQ_ERR_UNSUPPORTED;
     if (K % mq::kGroup || N % bn) return MQ_ERR_UNSUPPORTED;
-    if (K > (int64_t(1) << 30) || N > (int64_t(1) << 30) || N * K > (int64_t(1) << 40))
-        return MQ_ERR_UNSUPPORTED;
+    // K <= 65536: the kernels' per-row block tables hold up to 1024 column blocks
+    if (K > 65536 || N > (int64_t(1) << 30) || N * K > (int64_t(1) << 40)) return MQ_ERR_UNSUPPORTED;
     return MQ_OK;
 }
 
@@ -111,7 +111,7 @@ int mq_select_blocks(const float* w, const float* h, int64_t N, int64_t K, int g
     if (rc) return rc;
     const int64_t nb = (N / bn) * (K / bk);
     if (k_blocks < 0 || k_blocks > nb) return MQ_ERR_INVALID_ARG;
-    if (!w || !h || !row_ptr || !delta || (k_blocks > 0 && !col_idx) || !aligned16(w))
+    if (!w || !h || !row_ptr || !delta || (k_blocks > 0 && !col_idx) || !aligned16(w) || !aligned16(h))
         return MQ_ERR_INVALID_ARG;
     return hip_status(mq::launch_select(w, h, N, K, bn, k_blocks, row_ptr, col_idx, delta,
                                         static_cast<hipStream_t>(stream)));
@@ -122,7 +122,7 @@ int mq_pack_weights(const float* w, int64_t N, int64_t K, int group, int bn, int
                     uint16_t* sw, uint8_t* rq, void* stream) {
     int rc = check_layer(N, K, group, bn, bk);
     if (rc) return rc;
-    if (!w || !wq || !sw || !aligned16(w)) return MQ_ERR_INVALID_ARG;
+    if (!w || !wq || !sw || !aligned16(w) || !aligned16(wq)) return MQ_ERR_INVALID_ARG;
     rc = check_csr(row_ptr, col_idx, rq, nnz, N, K, bn, bk);
     if (rc) return rc;
     return hip_status(mq::launch_pack(w, N, K, bn, row_ptr, col_idx, nnz, wq, sw, rq,

@@ -23,32 +23,19 @@
 
 namespace mq {
 
-// Cursor over one block row's CSR list; advanced group by group. Values are the
-// same in every lane, so they live in scalar registers.
-struct Zipper {
-    int p, pend;
-    __device__ __forceinline__ void init(const int32_t* __restrict__ row_ptr,
-                                         const int32_t* __restrict__ col_idx, int nnz, int br,
-                                         int kb_start) {
-        const int lo = clampi(row_ptr[br], 0, nnz);
-        const int hi = clampi(row_ptr[br + 1], lo, nnz);
-        int a = lo, b = hi;
-        while (a < b) {
-            const int mid = (a + b) >> 1;
-            if (col_idx[mid] < kb_start) a = mid + 1; else b = mid;
-        }
-        p = a;
-        pend = hi;
+// The zipper: CSR positions of the residual blocks of one block row, for the
+// column blocks a wave walks, gathered into an LDS table in one parallel pass
+// (lane i reads list entry lo + i), so the K loop finds each group's blocks
+// with an LDS read instead of a chain of dependent loads.
+__device__ __forceinline__ void zip_table(const GemmArgs& a, int br, int kb0, int nkb, int* tab,
+                                          int lane, int nlanes) {
+    const int lo = clampi(a.row_ptr[br], 0, a.nnz);
+    const int hi = clampi(a.row_ptr[br + 1], lo, a.nnz);
+    for (int i = lo + lane; i < hi; i += nlanes) {
+        const int rel = a.col_idx[i] - kb0;
+        if (rel >= 0 && rel < nkb) tab[rel] = i;
     }
-    // CSR entries of the two column blocks of group g (or -1).
-    __device__ __forceinline__ void next(const int32_t* __restrict__ col_idx, int g, int& j0, int& j1) {
-        j0 = -1;
-        j1 = -1;
-        while (p < pend && col_idx[p] < 2 * g) ++p;   // only malformed lists take this
-        if (p < pend && col_idx[p] == 2 * g) j0 = p++;
-        if (p < pend && col_idx[p] == 2 * g + 1) j1 = p++;
-    }
-};
+}
 
 __device__ __forceinline__ void store_out(const GemmArgs& a, int OUTMODE, int m, int n, float v) {
     const int64_t idx = static_cast<int64_t>(m) * a.N + n;
@@ -65,14 +52,26 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int OUTMODE, int m,
 // Skinny kernel, M <= 32 (decode). A workgroup owns 16 output columns and all
 // tokens; its waves split the K groups and reduce through LDS in a fixed order.
 // Every weight byte is read by exactly one lane, with 16-byte loads; each lane
-// covers 32 consecutive K of one output row per group.
+// covers 32 consecutive K of one output row per group. A wave requests one
+// chunk of groups at a time; the bytes in flight per CU come from the many
+// workgroups that fit side by side (the kernel is kept small in registers).
 // ===========================================================================
-constexpr int kChunk = 4;      // groups whose loads are issued together
-constexpr int kMaxWaves = 16;
+constexpr int kChunk = 4;      // groups per load batch
+constexpr int kMaxWaves = 8;
+constexpr int kMaxWaveKb = 64; // column blocks one wave may walk (32 groups)
+
+template <int MT>
+struct SkinnyChunk {
+    uint4 bw[kChunk], rw[kChunk];
+    uint4 aw[kChunk][MT];
+    float sc[kChunk];
+    int rg;   // bit u: group gc + u holds a chosen block in this row
+};
 
 template <int MT, bool RES, bool DUMP, int OUTMODE>
-__global__ __launch_bounds__(1024) void k_gemm_skinny(GemmArgs a) {
+__global__ __launch_bounds__(512) void k_gemm_skinny(GemmArgs a) {
     __shared__ float red[kMaxWaves * MT * 256];
+    __shared__ int jtab[RES ? kMaxWaves * kMaxWaveKb : 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int li = lane & 15, kg = lane >> 4;
     const int G = a.K / kGroup;
@@ -90,8 +89,44 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny(GemmArgs a) {
     }
     const uint16_t* srow = a.sw + static_cast<int64_t>(n) * G;
     const int br = n0 / a.bn, rrow = n - br * a.bn;
-    Zipper z;
-    if (RES) z.init(a.row_ptr, a.col_idx, a.nnz, br, 2 * g0);
+    int* tab = jtab + (RES ? wave * kMaxWaveKb : 0);
+
+    auto load_base = [&](int gc, SkinnyChunk<MT>& c) {
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const int g = gc + u;
+            const bool ok = g < g1;
+            c.bw[u] = ok ? ldg16(wrow + g * 64) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) c.aw[u][t] = (ok && xv[t]) ? ldg16(xrow[t] + g * 64) : make_uint4(0, 0, 0, 0);
+            c.sc[u] = ok ? f16_bits_to_f32(srow[g]) : 0.0f;
+        }
+    };
+    auto load_res = [&](int gc, SkinnyChunk<MT>& c) {
+        c.rg = 0;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const int g = gc + u;
+            c.rw[u] = make_uint4(0, 0, 0, 0);
+            if (RES && g < g1) {
+                const int j0 = tab[2 * (g - g0)], j1 = tab[2 * (g - g0) + 1];
+                if (j0 >= 0 || j1 >= 0) c.rg |= 1 << u;
+                const int j = kg < 2 ? j0 : j1;
+                if (j >= 0) c.rw[u] = ldg16(a.rq + (static_cast<int64_t>(j) * a.bn + rrow) * 32 + (kg & 1) * 16);
+            }
+        }
+    };
+
+    SkinnyChunk<MT> cur;
+    load_base(g0, cur);
+    if (RES) {
+        tab[lane] = -1;
+        zip_table(a, br, 2 * g0, 2 * (g1 - g0), tab, lane, 64);
+        __syncthreads();
+        load_res(g0, cur);
+    } else {
+        cur.rg = 0;
+    }
 
     float acc[MT][4];
 #pragma unroll
@@ -99,46 +134,29 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
 
-    const uint4 zero4 = make_uint4(0, 0, 0, 0);
     for (int gc = g0; gc < g1; gc += kChunk) {
-        uint4 bw[kChunk], rw[kChunk], aw[kChunk][MT];
-        float sc[kChunk];
-        bool rg[kChunk];
-#pragma unroll
-        for (int u = 0; u < kChunk; ++u) {
-            const int g = gc + u;
-            const bool ok = g < g1;
-            bw[u] = ok ? ldg16(wrow + g * 64) : zero4;
-#pragma unroll
-            for (int t = 0; t < MT; ++t) aw[u][t] = (ok && xv[t]) ? ldg16(xrow[t] + g * 64) : zero4;
-            sc[u] = ok ? f16_bits_to_f32(srow[g]) : 0.0f;
-            rg[u] = false;
-            rw[u] = zero4;
-            if (RES && ok) {
-                int j0, j1;
-                z.next(a.col_idx, g, j0, j1);
-                rg[u] = (j0 >= 0) || (j1 >= 0);
-                const int j = kg < 2 ? j0 : j1;
-                if (j >= 0) rw[u] = ldg16(a.rq + (static_cast<int64_t>(j) * a.bn + rrow) * 32 + (kg & 1) * 16);
-            }
+        if (gc != g0) {
+            load_base(gc, cur);
+            if (RES) load_res(gc, cur);
         }
 #pragma unroll
         for (int u = 0; u < kChunk; ++u) {
             const int g = gc + u;
             if (g >= g1) break;
+            const bool res = RES && ((cur.rg >> u) & 1);
             v4i b0, b1;
             float scale;
-            if (RES && rg[u]) {
-                unpack_comb(bw[u], rw[u], b0, b1);
-                scale = (sc[u] / 14.0f) * 0.0625f;
+            if (res) {
+                unpack_comb(cur.bw[u], cur.rw[u], b0, b1);
+                scale = (cur.sc[u] / 14.0f) * 0.0625f;
             } else {
-                unpack16(bw[u], b0, b1);
-                scale = sc[u] * 0.00390625f;
+                unpack16(cur.bw[u], b0, b1);
+                scale = cur.sc[u] * 0.00390625f;
             }
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 v4i a0, a1;
-                unpack16(aw[u][t], a0, a1);
+                unpack16(cur.aw[u][t], a0, a1);
                 v4i c = v4i{0, 0, 0, 0};
                 c = mfma_i8(a0, b0, c);
                 c = mfma_i8(a1, b1, c);
@@ -150,7 +168,7 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny(GemmArgs a) {
                         const int m = t * 16 + kg * 4 + r;
                         if (m < a.M)
                             a.acc_dump[(static_cast<int64_t>(m) * a.N + n) * G + g] =
-                                (RES && rg[u]) ? (c[r] >> 4) : 14 * (c[r] >> 8);
+                                res ? (c[r] >> 4) : 14 * (c[r] >> 8);
                     }
                 }
             }
@@ -175,25 +193,27 @@ __global__ __launch_bounds__(1024) void k_gemm_skinny(GemmArgs a) {
 // ===========================================================================
 // Tiled kernel, M > 32 (prefill). 128 x 128 output tile per workgroup, four
 // waves of 64 x 64, one K group per step. The activation and base-weight tiles
-// of the next group are fetched into registers while the current group's
-// tiles are consumed from LDS (double buffer, one barrier per group).
+// of the next group, and the residual rows it needs, are fetched into registers
+// while the current group's tiles are consumed from LDS (double buffer, one
+// barrier per group).
 // ===========================================================================
 constexpr int kBM = 128, kBN = 128;
-constexpr int kRowB = 80;   // LDS bytes per tile row: 64 data + 16 pad (conflict-free b128 reads)
+constexpr int kRowB = 80;          // LDS bytes per tile row: 64 data + 16 pad (conflict-free b128 reads)
+constexpr int kMaxKb = 1024;       // column blocks per row the LDS zipper table holds (K <= 65536)
 
 template <bool RES, bool DUMP, int OUTMODE>
 __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
     __shared__ __align__(16) uint8_t As[2][kBM * kRowB];
     __shared__ __align__(16) uint8_t Bs[2][kBN * kRowB];
+    __shared__ int jtab[RES ? 2 * kMaxKb : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, kg = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
     const int tiles_n = (a.N + kBN - 1) / kBN;
     const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
     const int m0 = tm * kBM, n0 = tn * kBN;
-    const int G = a.K / kGroup;
+    const int G = a.K / kGroup, nbc = a.K / kBk;
     const int64_t Kh = a.K / 2;
-    const uint4 zero4 = make_uint4(0, 0, 0, 0);
 
     // global -> LDS assignment: 512 16-byte chunks per operand tile, two per thread
     int ld_row[2], ld_part[2];
@@ -211,12 +231,36 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
         ga[i] = a.xq + static_cast<int64_t>(va[i] ? m : 0) * Kh + ld_part[i] * 16;
         gb[i] = a.wq + static_cast<int64_t>(vb[i] ? nn : 0) * Kh + ld_part[i] * 16;
     }
-    uint4 ra[2], rb[2];
+    const int nw0 = n0 + wn * 64;                 // this wave's first output column
+    const bool wave_cols = nw0 < a.N;
+    const int br = nw0 / a.bn, rbase = nw0 - br * a.bn;
+    const int* tab = jtab + (RES ? wn * kMaxKb : 0);
+
+    uint4 ra[2], rb[2], rr[4];
+    float sn[4];
+    int rgrp_next = 0;
     auto fetch = [&](int g) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            ra[i] = va[i] ? ldg16(ga[i] + g * 64) : zero4;
-            rb[i] = vb[i] ? ldg16(gb[i] + g * 64) : zero4;
+            ra[i] = va[i] ? ldg16(ga[i] + g * 64) : make_uint4(0, 0, 0, 0);
+            rb[i] = vb[i] ? ldg16(gb[i] + g * 64) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int nn = nw0 + j * 16 + li;
+            sn[j] = nn < a.N ? f16_bits_to_f32(a.sw[static_cast<int64_t>(nn) * G + g]) : 0.0f;
+        }
+        if (RES) {
+            const int j0 = wave_cols ? tab[2 * g] : -1, j1 = wave_cols ? tab[2 * g + 1] : -1;
+            rgrp_next = (j0 >= 0) || (j1 >= 0);
+            const int jb = kg < 2 ? j0 : j1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int nn = nw0 + j * 16 + li;
+                rr[j] = (jb >= 0 && nn < a.N)
+                            ? ldg16(a.rq + (static_cast<int64_t>(jb) * a.bn + rbase + j * 16 + li) * 32 + (kg & 1) * 16)
+                            : make_uint4(0, 0, 0, 0);
+            }
         }
     };
     auto stash = [&](int buf) {
@@ -227,13 +271,14 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
         }
     };
 
-    const int nw0 = n0 + wn * 64;                 // this wave's first output column
-    const int br = nw0 / a.bn, rbase = nw0 - br * a.bn;
-    Zipper z;
     if (RES) {
-        z.p = 0;
-        z.pend = 0;
-        if (nw0 < a.N) z.init(a.row_ptr, a.col_idx, a.nnz, br, 0);
+        for (int i = tid; i < 2 * nbc; i += 256) jtab[(i / nbc) * kMaxKb + i % nbc] = -1;
+        __syncthreads();
+        // both wave columns' block rows (the same row when bn == 128)
+        const int brow0 = n0 / a.bn, brow1 = (n0 + 64) / a.bn;
+        if (n0 < a.N) zip_table(a, brow0, 0, nbc, jtab, tid, 256);
+        if (n0 + 64 < a.N) zip_table(a, brow1, 0, nbc, jtab + kMaxKb, tid, 256);
+        __syncthreads();
     }
 
     float acc[4][4][4];
@@ -246,33 +291,13 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
 
     fetch(0);
     stash(0);
+    uint4 rw[4] = {rr[0], rr[1], rr[2], rr[3]};
+    float sc[4] = {sn[0], sn[1], sn[2], sn[3]};
+    int rgrp = rgrp_next;
     __syncthreads();
     for (int g = 0; g < G; ++g) {
         const int buf = g & 1;
         if (g + 1 < G) fetch(g + 1);
-        float sc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int nn = nw0 + j * 16 + li;
-            sc[j] = nn < a.N ? f16_bits_to_f32(a.sw[static_cast<int64_t>(nn) * G + g]) : 0.0f;
-        }
-        bool rgrp = false;
-        uint4 rw[4] = {zero4, zero4, zero4, zero4};
-        if (RES) {
-            int j0, j1;
-            z.next(a.col_idx, g, j0, j1);
-            rgrp = (j0 >= 0) || (j1 >= 0);
-            const int jb = kg < 2 ? j0 : j1;
-            if (jb >= 0) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int nn = nw0 + j * 16 + li;
-                    if (nn < a.N)
-                        rw[j] = ldg16(a.rq + (static_cast<int64_t>(jb) * a.bn + rbase + j * 16 + li) * 32 +
-                                      (kg & 1) * 16);
-                }
-            }
-        }
         v4i a0[4], a1[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -310,7 +335,16 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
                 }
             }
         }
-        if (g + 1 < G) stash(buf ^ 1);
+        if (g + 1 < G) {
+            stash(buf ^ 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sc[j] = sn[j];
+            if (RES) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) rw[j] = rr[j];
+                rgrp = rgrp_next;
+            }
+        }
         __syncthreads();
     }
 

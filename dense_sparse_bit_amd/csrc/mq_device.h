@@ -48,18 +48,51 @@ __device__ __forceinline__ int rtn_code(float v, float s) {
     return static_cast<int>(t);
 }
 
-// One element of the decomposition W ~ s*q + s_r*r for a group with fp16 scale s.
+// rint(fl(v / s)) for s > 0 without a per-element division, given rs = fl(1 / s).
+// t = fl(v * rs) differs from the exact quotient by at most |v/s| * 2^-22.9, and
+// fl(v/s) by at most |v/s| * 2^-24, so for |t| <= 8 the two lie within 1.5e-6 of
+// each other. When t is farther than 4e-6 from every half-integer, no rounding
+// boundary separates them and rint(t) == rint(fl(v/s)); otherwise (or for larger
+// quotients) the correctly rounded quotient is formed. The result is therefore
+// identical to rintf(v / s). (A non-finite t, from a reciprocal that overflowed
+// for a subnormal s, fails both comparisons and also takes the exact path.)
+__device__ __forceinline__ float rint_quot(float v, float s, float rs) {
+    const float t = v * rs;
+    const float q = __builtin_rintf(t);
+    if (__builtin_expect(fabsf(t - q) < 0.5f - 4e-6f && fabsf(t) <= 8.0f, 1)) return q;
+    return __builtin_rintf(v / s);
+}
+
+// Symmetric RTN code as a float: 0 when s == 0, else clamp(rint(v / s), -7, 7).
+__device__ __forceinline__ float rtn_codef(float v, float s, float rs) {
+    if (s == 0.0f) return 0.0f;
+    return fminf(fmaxf(rint_quot(v, s, rs), -7.0f), 7.0f);
+}
+
+// Per-group constants of the decomposition W ~ s*q + s_r*r for an fp16 scale s.
+struct GroupScale {
+    float s, rs, sr, rsr;   // s, 1/s, s_r = s/14, 1/s_r (all correctly rounded)
+};
+__device__ __forceinline__ GroupScale group_scale(float s) {
+    GroupScale g;
+    g.s = s;
+    g.sr = s / 14.0f;
+    g.rs = s == 0.0f ? 0.0f : 1.0f / s;
+    g.rsr = s == 0.0f ? 0.0f : 1.0f / g.sr;
+    return g;
+}
+
+// One element: base code q, E = w - s*q, residual code r, E' = E - s_r*r.
 struct Elem {
-    int q, r;
+    float q, r;
     float e, ep;
 };
-__device__ __forceinline__ Elem quant_elem(float w, float s) {
+__device__ __forceinline__ Elem quant_elem(float w, const GroupScale& g) {
     Elem o;
-    o.q = rtn_code(w, s);
-    o.e = __builtin_fmaf(-s, static_cast<float>(o.q), w);
-    const float sr = s / 14.0f;
-    o.r = rtn_code(o.e, sr);
-    o.ep = __builtin_fmaf(-sr, static_cast<float>(o.r), o.e);
+    o.q = rtn_codef(w, g.s, g.rs);
+    o.e = __builtin_fmaf(-g.s, o.q, w);
+    o.r = rtn_codef(o.e, g.sr, g.rsr);
+    o.ep = __builtin_fmaf(-g.sr, o.r, o.e);
     return o;
 }
 

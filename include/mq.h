@@ -18,12 +18,12 @@
  *     must not overlap.
  *   - int4 data are two's-complement nibbles, the low nibble of each byte holds
  *     the even index, rows are contiguous (row-major).
- *   - Packed buffers (xq, wq, rq) must be 16-byte aligned.
+ *   - Packed buffers (xq, wq, rq) and the fp32 w and h must be 16-byte aligned.
  *   - Argument checks happen before any launch and return MQ_ERR_INVALID_ARG or
  *     MQ_ERR_UNSUPPORTED with nothing written. A failed launch returns
  *     MQ_ERR_HIP; faults inside a kernel surface at the caller's next
  *     synchronisation of `stream`.
- *   - Shapes the GPU path supports: K % 128 == 0, group == 128, bk == 64,
+ *   - Shapes the GPU path supports: K % 128 == 0, K <= 65536, group == 128, bk == 64,
  *     bn in {64, 128}, N % bn == 0. M may be any value >= 0 (M == 0 is a no-op).
  *   - Inputs must be finite, and max|w| over a group must be below 7 * 65504
  *     (the fp16 scale must be finite); otherwise results are unspecified.

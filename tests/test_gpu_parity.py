@@ -239,3 +239,32 @@ def test_zero_tokens_no_op(mq):
     y = mq.gemm_w4a4_residual(xq, sx, wq, sw, rp, none, none, 512, bn=64)
     torch.cuda.synchronize()
     assert y.shape == (0, 128)
+
+
+def test_quantizer_near_ties(mq, orc):
+    """Quotients on and next to half-integers, where a division-free quotient
+    would round the other way: base codes (w / s), residual codes (E / s_r) and
+    activation codes (x / s_x) must still equal the oracle's correctly rounded
+    divisions, bit for bit, through the whole path."""
+    import torch
+    rng = np.random.default_rng(77)
+    N, K, M = 128, 512, 8
+    cfg = synth.custom_config("near_ties", M=M, K=K, N=N, bn=64, x_bf16=False)
+    s = np.float32(2.0) ** rng.integers(-12, 0, size=(N, K // 128)).astype(np.float32)
+    sr = (s / np.float32(14)).astype(np.float32)
+    k = rng.integers(-7, 7, size=(N, K)).astype(np.float32)
+    j = rng.integers(-7, 7, size=(N, K)).astype(np.float32)
+    S = np.repeat(s, 128, axis=1)
+    SR = np.repeat(sr, 128, axis=1)
+    kind = rng.integers(0, 4, size=(N, K))
+    w = np.where(kind == 0, S * (k + np.float32(0.5)),                       # exact base ties
+        np.where(kind == 1, np.nextafter(S * (k + np.float32(0.5)), np.float32(np.inf)),
+        np.where(kind == 2, S * k + SR * (j + np.float32(0.5)),                # residual near-ties
+                 np.nextafter(S * k + SR * (j + np.float32(0.5)), np.float32(-np.inf))))).astype(np.float32)
+    w[:, ::128] = np.float32(7.0) * S[:, ::128]                               # absmax 7s -> scale s
+    x = (rng.integers(-7, 7, size=(M, K)).astype(np.float32) + np.float32(0.5))
+    x[:, 1::3] = np.nextafter(x[:, 1::3], np.float32(0))
+    x[:, 0] = 7.0                                                             # s_x = 1
+    inp = synth.Inputs(cfg, w, x, None)
+    _check(mq, orc, inp, cfg.k_blocks(100), "f32")
+    _check(mq, orc, inp, cfg.k_blocks(10), "bf16")
