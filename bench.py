@@ -88,10 +88,11 @@ def bench_step(mq, torch, cfg, inp, k_blocks, steps, warmup):
     sel_out = (torch.empty(N // bn + 1, dtype=torch.int32, device=dev),
                torch.empty(max(k_blocks, 1), dtype=torch.int32, device=dev),
                torch.empty(nb, dtype=torch.float64, device=dev))
-    pack_out = (torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
-                torch.empty((N, K // 128), dtype=torch.int16, device=dev),
+    G = K // 128
+    pack_out = (torch.empty((N // 16, G, 1024), dtype=torch.uint8, device=dev),
+                torch.empty((N // 16, (G + 3) // 4, 16, 4), dtype=torch.int16, device=dev),
                 torch.empty((max(k_blocks, 1), bn, 32), dtype=torch.uint8, device=dev))
-    xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    xq = torch.empty((G, M, 64), dtype=torch.uint8, device=dev)
     sx = torch.empty(M, dtype=torch.float32, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     names = ["hessian_diag", "select_blocks", "pack_weights", "quantize_act", "gemm_w4a4_residual"]

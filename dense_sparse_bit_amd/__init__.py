@@ -3,8 +3,12 @@
 The functions below only marshal torch device tensors (pointers, sizes and the
 current HIP stream) into ``libmq.so``; every step of the computation runs in the
 library's HIP kernels. There is no CPU fallback: importing this package raises
-if the library has not been built (``python -m dense_sparse_bit_amd._build``),
+if the library has not been built (``python dense_sparse_bit_amd/_build.py``),
 and every call raises :class:`MQError` on a non-zero status.
+
+Packed tensors use the library's device layouts (include/mq.h): xq is
+[K/128][M][64] bytes (group-major), wq is [N/16][K/128][1024] bytes (16-row x
+1-group tiles), sw is [N/16][ceil(K/512)][16][4] fp16 bits.
 """
 from __future__ import annotations
 
@@ -20,7 +24,7 @@ MQ_F32, MQ_BF16 = 0, 1
 GROUP, BK = 128, 64
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m dense_sparse_bit_amd._build` "
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python dense_sparse_bit_amd/_build.py` "
                       "(hipcc, gfx950). There is no fallback implementation.")
 
 _lib = C.CDLL(LIB_PATH)
@@ -32,10 +36,10 @@ _SIGS = {
     "mq_select_blocks": [_p, _p, _i64, _i64, _int, _int, _int, _i64, _p, _p, _p, _p],
     "mq_pack_weights": [_p, _i64, _i64, _int, _int, _int, _p, _p, _i64, _p, _p, _p, _p],
     "mq_gemm_w4a4_residual": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
-                              _p, _int, _p, _p],
-    "mq_gemm_w4a4_dense": [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p, _int, _p, _p],
+                              _p, _int, _p, _p, C.c_size_t, _p],
+    "mq_gemm_w4a4_dense": [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p, _int, _p, _p, C.c_size_t, _p],
     "mq_gemm_residual_separate": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int,
-                                  _int, _p, _int, _p, _p],
+                                  _int, _p, _int, _p, _p, C.c_size_t, _p],
 }
 for _name, _args in _SIGS.items():
     getattr(_lib, _name).argtypes = _args
@@ -44,8 +48,10 @@ _lib.mq_status_string.argtypes = [C.c_int]
 _lib.mq_status_string.restype = C.c_char_p
 _lib.mq_version.argtypes = []
 _lib.mq_version.restype = C.c_int
+_lib.mq_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64]
+_lib.mq_gemm_workspace_bytes.restype = C.c_size_t
 
-EXPORTS = tuple(_SIGS) + ("mq_status_string", "mq_version")
+EXPORTS = tuple(_SIGS) + ("mq_status_string", "mq_version", "mq_gemm_workspace_bytes")
 
 
 class MQError(RuntimeError):
@@ -111,10 +117,11 @@ def hessian_diag(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) 
 # --------------------------------------------------------------------------- a4
 def quantize_act(x: torch.Tensor, xq: torch.Tensor | None = None, sx: torch.Tensor | None = None,
                  stream=None):
+    """Returns (xq u8 [K/128][M][64], sx fp32 [M])."""
     _device_contig(x, "x")
     M, K = x.shape
     if xq is None:
-        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        xq = torch.empty((K // GROUP, M, 64), dtype=torch.uint8, device=x.device)
     if sx is None:
         sx = torch.empty(M, dtype=torch.float32, device=x.device)
     _call("mq_quantize_act", _ptr(x), _x_dtype(x), M, K, _ptr(xq), _ptr(sx), _stream(stream))
@@ -143,13 +150,15 @@ def select_blocks(w: torch.Tensor, h: torch.Tensor, k_blocks: int, bn: int = 64,
 # --------------------------------------------------------------------------- a1 + a3
 def pack_weights(w: torch.Tensor, row_ptr: torch.Tensor, col_idx: torch.Tensor, bn: int = 64,
                  group: int = GROUP, bk: int = BK, out=None, stream=None):
-    """Returns (wq u8 [N][K/2], sw fp16-bits int16 [N][K/group], rq u8 [nnz][bn][bk/2])."""
+    """Returns (wq u8 [N/16][G][1024], sw fp16-bits int16 [N/16][G4][16][4],
+    rq u8 [nnz][bn][bk/2]) with G = K/128, G4 = ceil(G/4)."""
     _device_contig(w, "w")
     N, K = w.shape
     nnz = int(col_idx.numel())
     if out is None:
-        wq = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
-        sw = torch.empty((N, K // group), dtype=torch.int16, device=w.device)
+        G = K // group
+        wq = torch.empty((N // 16, G, 1024), dtype=torch.uint8, device=w.device)
+        sw = torch.empty((N // 16, (G + 3) // 4, 16, 4), dtype=torch.int16, device=w.device)
         rq = torch.empty((max(nnz, 1), bn, bk // 2), dtype=torch.uint8, device=w.device)
     else:
         wq, sw, rq = out
@@ -168,40 +177,70 @@ def _y_dtype(dtype) -> int:
     raise TypeError(f"output must be float32 or bfloat16, got {dtype}")
 
 
+def _gemm_mn(sx, wq, K: int):
+    """(M, N) of a GEMM call: M tokens from sx, N outputs from the packed weight bytes."""
+    if K <= 0 or (wq.numel() * 2) % K:
+        raise ValueError(f"wq holds {wq.numel()} bytes, not a multiple of K/2 = {K // 2}")
+    return int(sx.numel()), int(wq.numel() * 2 // K)
+
+
+def workspace_bytes(M: int, N: int, K: int) -> int:
+    """Device bytes of split-K partials the GEMM calls need for this shape."""
+    return int(_lib.mq_gemm_workspace_bytes(M, N, K))
+
+
+def workspace(M: int, N: int, K: int, device="cuda"):
+    """A workspace tensor for the GEMM calls of this shape (None if none is needed)."""
+    n = workspace_bytes(M, N, K)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _ws_args(workspace_t, M, N, K, device):
+    if workspace_t is None:
+        workspace_t = workspace(M, N, K, device)
+    if workspace_t is None:
+        return None, 0, None
+    return _ptr(workspace_t), workspace_t.numel() * workspace_t.element_size(), workspace_t
+
+
 def gemm_w4a4_residual(xq, sx, wq, sw, row_ptr, col_idx, rq, K: int, bn: int = 64,
-                       out_dtype=torch.bfloat16, y=None, acc_dump=None, stream=None):
+                       out_dtype=torch.bfloat16, y=None, acc_dump=None, workspace=None,
+                       stream=None):
     """Fused dense + sparse-residual W4A4 GEMM. acc_dump: optional int32 [M][N][K/128]."""
-    M, N = xq.shape[0], wq.shape[0]
+    M, N = _gemm_mn(sx, wq, K)
     nnz = int(col_idx.numel())
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=wq.device)
+    wp, wb, _keep = _ws_args(workspace, M, N, K, wq.device)
     _call("mq_gemm_w4a4_residual", _ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(row_ptr),
           _ptr(col_idx) if nnz else None, _ptr(rq) if nnz else None, nnz, M, N, K, GROUP, bn, BK,
-          _ptr(y), _y_dtype(y.dtype), _ptr(acc_dump), _stream(stream))
+          _ptr(y), _y_dtype(y.dtype), _ptr(acc_dump), wp, wb, _stream(stream))
     return y
 
 
 def gemm_w4a4_dense(xq, sx, wq, sw, K: int, out_dtype=torch.bfloat16, y=None, acc_dump=None,
-                    stream=None):
-    M, N = xq.shape[0], wq.shape[0]
+                    workspace=None, stream=None):
+    M, N = _gemm_mn(sx, wq, K)
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=wq.device)
+    wp, wb, _keep = _ws_args(workspace, M, N, K, wq.device)
     _call("mq_gemm_w4a4_dense", _ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, GROUP, _ptr(y),
-          _y_dtype(y.dtype), _ptr(acc_dump), _stream(stream))
+          _y_dtype(y.dtype), _ptr(acc_dump), wp, wb, _stream(stream))
     return y
 
 
 def gemm_residual_separate(xq, sx, wq, sw, row_ptr, col_idx, rq, K: int, bn: int = 64,
-                           out_dtype=torch.bfloat16, y=None, ws=None, stream=None):
-    M, N = xq.shape[0], wq.shape[0]
+                           out_dtype=torch.bfloat16, y=None, ws=None, workspace=None, stream=None):
+    M, N = _gemm_mn(sx, wq, K)
     nnz = int(col_idx.numel())
     if y is None:
         y = torch.empty((M, N), dtype=out_dtype, device=wq.device)
     if ws is None:
         ws = torch.empty((M, N), dtype=torch.float32, device=wq.device)
+    wp, wb, _keep = _ws_args(workspace, M, N, K, wq.device)
     _call("mq_gemm_residual_separate", _ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(row_ptr),
           _ptr(col_idx) if nnz else None, _ptr(rq) if nnz else None, nnz, M, N, K, GROUP, bn, BK,
-          _ptr(y), _y_dtype(y.dtype), _ptr(ws), _stream(stream))
+          _ptr(y), _y_dtype(y.dtype), _ptr(ws), wp, wb, _stream(stream))
     return y
 
 

@@ -1,9 +1,10 @@
 """Build libmq.so (the HIP library) in-tree with hipcc for gfx950.
 
-    python -m dense_sparse_bit_amd._build
+    python dense_sparse_bit_amd/_build.py
 
-Cross-compiles without a GPU. Objects go to dense_sparse_bit_amd/_build/,
-the shared library to dense_sparse_bit_amd/libmq.so.
+A standalone script (it imports nothing from the package, whose import needs the
+built library). Cross-compiles without a GPU. Objects go to
+dense_sparse_bit_amd/_build/, the shared library to dense_sparse_bit_amd/libmq.so.
 """
 from __future__ import annotations
 

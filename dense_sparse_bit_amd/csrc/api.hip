@@ -34,7 +34,7 @@ int check_gemm(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint
     if (bad_dtype(y_dtype)) return MQ_ERR_INVALID_ARG;
     if (M > 0 && (!xq || !sx || !y)) return MQ_ERR_INVALID_ARG;
     if (!wq || !sw) return MQ_ERR_INVALID_ARG;
-    if (!aligned16(xq) || !aligned16(wq)) return MQ_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(wq) || (reinterpret_cast<uintptr_t>(sw) & 7u)) return MQ_ERR_INVALID_ARG;
     // every int32 index the kernels form must fit
     if (M * N > (int64_t(1) << 31) - 1 || M * N * (K / mq::kGroup) > (int64_t(1) << 40))
         return MQ_ERR_UNSUPPORTED;
@@ -98,7 +98,7 @@ int mq_hessian_diag(const void* x, int x_dtype, int64_t M, int64_t K, float* h, 
 int mq_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* xq, float* sx,
                     void* stream) {
     if (M < 0 || K <= 0 || (K & 1) || bad_dtype(x_dtype)) return MQ_ERR_INVALID_ARG;
-    if (M > (int64_t(1) << 31) - 1 || M * K > (int64_t(1) << 40)) return MQ_ERR_UNSUPPORTED;
+    if (K % mq::kGroup || M > (int64_t(1) << 31) - 1 || M * K > (int64_t(1) << 40)) return MQ_ERR_UNSUPPORTED;
     if (M == 0) return MQ_OK;
     if (!x || !xq || !sx) return MQ_ERR_INVALID_ARG;
     return hip_status(mq::launch_quant_act(x, x_dtype == MQ_BF16, M, K, xq, sx, static_cast<hipStream_t>(stream)));
@@ -129,10 +129,42 @@ int mq_pack_weights(const float* w, int64_t N, int64_t K, int group, int bn, int
                                       static_cast<hipStream_t>(stream)));
 }
 
+size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || N % 64 || K % mq::kGroup || K > 65536) return 0;
+    return mq::gemm_workspace_bytes(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Runs `launch(part)` with the split-K partial buffer the shape needs: the
+// caller's workspace if given (and large enough), else a stream-ordered
+// allocation released on the same stream.
+template <class F>
+int with_workspace(int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, hipStream_t st,
+                   F launch) {
+    const size_t need = mq::gemm_workspace_bytes(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+    if (need == 0 || workspace) {
+        if (need > 0 && workspace_bytes < need) return MQ_ERR_INVALID_ARG;
+        return hip_status(launch(static_cast<float*>(workspace)));
+    }
+    float* tmp = nullptr;
+    if (hipMallocAsync(reinterpret_cast<void**>(&tmp), need, st) != hipSuccess) return MQ_ERR_HIP;
+    const hipError_t e = launch(tmp);
+    const hipError_t f = hipFreeAsync(tmp, st);
+    return (e == hipSuccess && f == hipSuccess) ? MQ_OK : MQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
 int mq_gemm_w4a4_residual(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint16_t* sw,
                           const int32_t* row_ptr, const int32_t* col_idx, const uint8_t* rq,
                           int64_t nnz, int64_t M, int64_t N, int64_t K, int group, int bn, int bk,
-                          void* y, int y_dtype, int32_t* acc_dump, void* stream) {
+                          void* y, int y_dtype, int32_t* acc_dump, void* workspace,
+                          size_t workspace_bytes, void* stream) {
     int rc = check_gemm(xq, sx, wq, sw, M, N, K, group, bn, bk, y, y_dtype);
     if (rc) return rc;
     rc = check_csr(row_ptr, col_idx, rq, nnz, N, K, bn, bk);
@@ -140,25 +172,29 @@ int mq_gemm_w4a4_residual(const uint8_t* xq, const float* sx, const uint8_t* wq,
     if (M == 0) return MQ_OK;
     const mq::GemmArgs a = make_args(xq, sx, wq, sw, row_ptr, col_idx, rq, nnz, M, N, K, bn, y, y_dtype,
                                      acc_dump, nullptr);
-    return hip_status(mq::launch_gemm(a, mq::GemmKind::Fused, static_cast<hipStream_t>(stream)));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    return with_workspace(M, N, K, workspace, workspace_bytes, st,
+                          [&](float* part) { return mq::launch_gemm(a, mq::GemmKind::Fused, part, st); });
 }
 
 int mq_gemm_w4a4_dense(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint16_t* sw,
                        int64_t M, int64_t N, int64_t K, int group, void* y, int y_dtype,
-                       int32_t* acc_dump, void* stream) {
+                       int32_t* acc_dump, void* workspace, size_t workspace_bytes, void* stream) {
     int rc = check_gemm(xq, sx, wq, sw, M, N, K, group, 64, mq::kBk, y, y_dtype);
     if (rc) return rc;
     if (M == 0) return MQ_OK;
     const mq::GemmArgs a = make_args(xq, sx, wq, sw, nullptr, nullptr, nullptr, 0, M, N, K, 64, y, y_dtype,
                                      acc_dump, nullptr);
-    return hip_status(mq::launch_gemm(a, mq::GemmKind::Dense, static_cast<hipStream_t>(stream)));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    return with_workspace(M, N, K, workspace, workspace_bytes, st,
+                          [&](float* part) { return mq::launch_gemm(a, mq::GemmKind::Dense, part, st); });
 }
 
 int mq_gemm_residual_separate(const uint8_t* xq, const float* sx, const uint8_t* wq,
                               const uint16_t* sw, const int32_t* row_ptr, const int32_t* col_idx,
                               const uint8_t* rq, int64_t nnz, int64_t M, int64_t N, int64_t K,
                               int group, int bn, int bk, void* y, int y_dtype, float* ws,
-                              void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream) {
     int rc = check_gemm(xq, sx, wq, sw, M, N, K, group, bn, bk, y, y_dtype);
     if (rc) return rc;
     rc = check_csr(row_ptr, col_idx, rq, nnz, N, K, bn, bk);
@@ -168,9 +204,10 @@ int mq_gemm_residual_separate(const uint8_t* xq, const float* sx, const uint8_t*
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const mq::GemmArgs a = make_args(xq, sx, wq, sw, row_ptr, col_idx, rq, nnz, M, N, K, bn, y, y_dtype,
                                      nullptr, ws);
-    hipError_t e = mq::launch_gemm(a, mq::GemmKind::DenseToWorkspace, st);
-    if (e != hipSuccess) return MQ_ERR_HIP;
-    return hip_status(mq::launch_residual_merge(a, st));
+    return with_workspace(M, N, K, workspace, workspace_bytes, st, [&](float* part) {
+        hipError_t e = mq::launch_gemm(a, mq::GemmKind::DenseToWorkspace, part, st);
+        return e != hipSuccess ? e : mq::launch_residual_merge(a, st);
+    });
 }
 
 }  // extern "C"

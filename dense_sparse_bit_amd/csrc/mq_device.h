@@ -141,4 +141,24 @@ __device__ __forceinline__ uint4 ldg16(const uint8_t* p) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// ---- device layouts of the packed operands --------------------------------
+// Every 64-lane load of a GEMM operand is 1 KB of contiguous memory in MFMA lane
+// order, so each request the vector memory pipeline carries is fully used:
+//   wq  [N/16][G][64][16 B]  tile (nt, g) holds rows 16nt..16nt+15 of group g;
+//                            lane l = 16*kc + r owns row 16nt + r, bytes
+//                            16kc..16kc+15 of that row's 64-byte group chunk
+//   sw  [N/16][G4][16][4]    fp16 group scales, G4 = ceil(G/4): one 8-byte load
+//                            gives a row the scales of four consecutive groups;
+//                            slots of groups >= G hold zero
+//   xq  [G][M][64 B]         group-major activations: a group's rows are
+//                            contiguous, so 16 tokens x 128 inputs is one 1 KB run
+__device__ __forceinline__ int64_t wq_tile(int64_t nt, int64_t G, int64_t g) { return (nt * G + g) * 1024; }
+__device__ __forceinline__ int64_t wq_byte(int64_t n, int64_t G, int64_t g, int kc) {
+    return wq_tile(n >> 4, G, g) + (kc * 16 + (n & 15)) * 16;
+}
+__device__ __forceinline__ int64_t sw_index(int64_t n, int64_t G4, int64_t g) {
+    return (((n >> 4) * G4 + (g >> 2)) * 16 + (n & 15)) * 4 + (g & 3);
+}
+__device__ __forceinline__ int64_t xq_row(int64_t g, int64_t M, int64_t m) { return (g * M + m) * 64; }
+
 }  // namespace mq

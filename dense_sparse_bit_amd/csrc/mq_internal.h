@@ -24,6 +24,14 @@ struct GemmArgs {
 
 enum class GemmKind { Fused, Dense, DenseToWorkspace };
 
+// How the decode GEMM (M <= 32) is split: nw waves per workgroup share K.
+struct DecodePlan {
+    int nw;
+};
+DecodePlan plan_decode(int M, int N, int K);
+// device workspace the GEMM of this shape needs (0 if none)
+size_t gemm_workspace_bytes(int M, int N, int K);
+
 hipError_t launch_hessian(const void* x, int bf16, int64_t M, int64_t K, float* h, hipStream_t st);
 hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, uint8_t* xq, float* sx,
                             hipStream_t st);
@@ -33,7 +41,7 @@ hipError_t launch_select(const float* w, const float* h, int64_t N, int64_t K, i
 hipError_t launch_pack(const float* w, int64_t N, int64_t K, int bn, const int32_t* row_ptr,
                        const int32_t* col_idx, int64_t nnz, uint8_t* wq, uint16_t* sw, uint8_t* rq,
                        hipStream_t st);
-hipError_t launch_gemm(const GemmArgs& a, GemmKind kind, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs& a, GemmKind kind, float* part, hipStream_t st);
 hipError_t launch_residual_merge(const GemmArgs& a, hipStream_t st);
 
 }  // namespace mq

@@ -59,7 +59,8 @@ __global__ __launch_bounds__(256) void k_hessian(const void* __restrict__ x, int
 // ---------------------------------------------------------------------------
 // a4: per-token symmetric int4 quantization. One workgroup per token; each
 // thread keeps its pairs of values in registers between the exact max-reduction
-// of |x| (order-free) and the quantization, so x is read once.
+// of |x| (order-free) and the quantization, so x is read once. Codes are stored
+// group-major ([K/128][M][64 B]), the layout the GEMM loads from.
 // ---------------------------------------------------------------------------
 constexpr int kQaRegs = 16;     // pairs kept in registers per thread (K <= 8192 read once)
 
@@ -71,7 +72,7 @@ __device__ __forceinline__ float2 load_pair(const void* x, bool bf16, int64_t j)
     return static_cast<const float2*>(x)[j];
 }
 
-__global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, int bf16, int64_t K,
+__global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, int bf16, int64_t M, int64_t K,
                                                    uint8_t* __restrict__ xq, float* __restrict__ sx) {
     const int64_t m = blockIdx.x, P = K / 2;
     const void* row = bf16 ? static_cast<const void*>(static_cast<const uint16_t*>(x) + m * K)
@@ -97,16 +98,17 @@ __global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, i
     const float s = a / 7.0f;
     const float rs = s == 0.0f ? 0.0f : 1.0f / s;
     if (t == 0) sx[m] = s;
-    uint8_t* out = xq + m * P;
+    // group-major output: byte j of the row (inputs 2j, 2j+1) goes to group j/64
     auto code = [&](float v) { return static_cast<int>(rtn_codef(v, s, rs)) & 15; };
+    auto dst = [&](int64_t j) { return xq + xq_row(j >> 6, M, m) + (j & 63); };
 #pragma unroll
     for (int i = 0; i < kQaRegs; ++i) {
         const int64_t j = t + 256 * i;
-        if (j < P) out[j] = static_cast<uint8_t>(code(v[i].x) | (code(v[i].y) << 4));
+        if (j < P) *dst(j) = static_cast<uint8_t>(code(v[i].x) | (code(v[i].y) << 4));
     }
     for (int64_t j = t + 256 * kQaRegs; j < P; j += 256) {
         const float2 u = load_pair(row, bf16, j);
-        out[j] = static_cast<uint8_t>(code(u.x) | (code(u.y) << 4));
+        *dst(j) = static_cast<uint8_t>(code(u.x) | (code(u.y) << 4));
     }
 }
 
@@ -261,9 +263,9 @@ __global__ __launch_bounds__(1024) void k_csr(const int32_t* __restrict__ rank, 
 // ---------------------------------------------------------------------------
 // a1 + a3: pack. One workgroup per (block row, group), 64 rows per pass, four
 // lanes per row with 32 weights each (eight 16-byte loads, one 16-byte store of
-// codes). The block row's CSR list is searched once, in parallel, for the two
-// column blocks of the group; chosen blocks get their 16-byte residual rows
-// written at their CSR position. W is read exactly once.
+// codes into the tiled wq layout). The block row's CSR list is searched once, in
+// parallel, for the two column blocks of the group; chosen blocks get their
+// 16-byte residual rows written at their CSR position. W is read exactly once.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t pack8(const int* c) {
     uint32_t v = 0;
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64
                                               uint8_t* __restrict__ wq, uint16_t* __restrict__ sw,
                                               uint8_t* __restrict__ rq) {
     __shared__ int pos[2];
-    const int64_t br = blockIdx.x, g = blockIdx.y, G = K / kGroup;
+    const int64_t br = blockIdx.x, g = blockIdx.y, G = K / kGroup, G4 = (G + 3) / 4;
     const int t = threadIdx.x, row = t >> 2, qd = t & 3;
     // first 64 rows' weights are requested before the list search, so the two
     // latencies overlap
@@ -332,9 +334,14 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64
             qc[i] = static_cast<int>(o.q);
             rc[i] = static_cast<int>(o.r);
         }
-        *reinterpret_cast<uint4*>(wq + n * (K / 2) + g * (kGroup / 2) + qd * 16) =
+        // tiled base codes: a wavefront's 16 rows x 4 quarters are one 1 KB tile
+        *reinterpret_cast<uint4*>(wq + wq_byte(n, G, g, qd)) =
             make_uint4(pack8(qc), pack8(qc + 8), pack8(qc + 16), pack8(qc + 24));
-        if (qd == 0) sw[n * G + g] = sb;
+        if (qd == 0) {
+            sw[sw_index(n, G4, g)] = sb;
+            if (g == G - 1)
+                for (int64_t gp = G; gp < 4 * G4; ++gp) sw[sw_index(n, G4, gp)] = 0;   // padding slots
+        }
         if (p >= 0)
             *reinterpret_cast<uint4*>(rq + (static_cast<int64_t>(p) * bn + r0 + row) * (kBk / 2) + (qd & 1) * 16) =
                 make_uint4(pack8(rc), pack8(rc + 8), pack8(rc + 16), pack8(rc + 24));
@@ -352,7 +359,7 @@ hipError_t launch_hessian(const void* x, int bf16, int64_t M, int64_t K, float* 
 
 hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, uint8_t* xq, float* sx,
                             hipStream_t st) {
-    k_quant_act<<<dim3(static_cast<unsigned>(M)), dim3(256), 0, st>>>(x, bf16, K, xq, sx);
+    k_quant_act<<<dim3(static_cast<unsigned>(M)), dim3(256), 0, st>>>(x, bf16, M, K, xq, sx);
     return hipGetLastError();
 }
 

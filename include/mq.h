@@ -16,9 +16,22 @@
  *     asynchronous on it unless stated otherwise.
  *   - Inputs are read-only. Outputs are fully overwritten. Inputs and outputs
  *     must not overlap.
- *   - int4 data are two's-complement nibbles, the low nibble of each byte holds
- *     the even index, rows are contiguous (row-major).
- *   - Packed buffers (xq, wq, rq) and the fp32 w and h must be 16-byte aligned.
+ *   - int4 data are two's-complement nibbles; the low nibble of each byte holds
+ *     the even input index.
+ *   - Packed layouts (G = K/128 groups, G4 = ceil(G/4)). Each is chosen so that one
+ *     64-lane 16-byte load of the GEMM reads 1 KB of contiguous memory:
+ *       xq  activations, group-major: byte (g, m, j) at (g*M + m)*64 + j holds
+ *           inputs k = 128g + 2j (low nibble) and 128g + 2j + 1 of token m.
+ *       wq  base codes, tiled by 16 rows x 1 group: row n, group g, byte j (0..63)
+ *           of the row's 64-byte group chunk is at
+ *             ((n/16)*G + g)*1024 + ((j/16)*16 + n%16)*16 + j%16.
+ *       sw  fp16 group scales, four groups per row entry: scale (n, g) is element
+ *             (((n/16)*G4 + g/4)*16 + n%16)*4 + g%4   of a u16 array of N*G4*4;
+ *           entries of groups g >= G are zero.
+ *       rq  residual codes of the chosen blocks, [nnz][bn][bk/2], rows contiguous.
+ *     Sizes: xq M*K/2 bytes, wq N*K/2 bytes, sw N*G4*4 u16, rq nnz*bn*bk/2 bytes.
+ *   - Packed buffers (xq, wq, rq) and the fp32 w and h must be 16-byte aligned;
+ *     sw must be 8-byte aligned.
  *   - Argument checks happen before any launch and return MQ_ERR_INVALID_ARG or
  *     MQ_ERR_UNSUPPORTED with nothing written. A failed launch returns
  *     MQ_ERR_HIP; faults inside a kernel surface at the caller's next
@@ -31,6 +44,7 @@
 #ifndef MQ_H
 #define MQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -66,7 +80,8 @@ int mq_hessian_diag(const void* x, int x_dtype, int64_t M, int64_t K, float* h, 
  * pipeline, Methodology 3).
  *   sx[m] = fp32(max_k |x[m][k]| / 7)
  *   xq[m][k] = sx[m] == 0 ? 0 : clamp(rint(x[m][k] / sx[m]), -7, 7)   (ties to even)
- * x: [M][K] fp32 or bf16, xq: u8 [M][K/2], sx: fp32 [M]. K even.
+ * x: [M][K] fp32 or bf16 (row-major), xq: M*K/2 bytes in the group-major layout
+ * above, sx: fp32 [M]. K % 128 == 0.
  */
 int mq_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* xq, float* sx,
                     void* stream);
@@ -94,12 +109,12 @@ int mq_select_blocks(const float* w, const float* h, int64_t N, int64_t K, int g
 /*
  * Packs the dense 4-bit base for every group and the 4-bit residual payload for
  * the chosen blocks (Methodology 1: W^ ~ Q(W^) + R, both parts 4-bit).
- *   sw[n][g] = fp16_rne( fp32(max_{k in g} |w[n][k]|) / 7 )      (fp16 bits)
- *   wq[n][k] = s == 0 ? 0 : clamp(rint(w / s), -7, 7)  with s = fp32(sw[n][g])
+ *   sw(n, g) = fp16_rne( fp32(max_{k in g} |w[n][k]|) / 7 )      (fp16 bits)
+ *   wq(n, k) = s == 0 ? 0 : clamp(rint(w / s), -7, 7)  with s = fp32(sw(n, g))
  *   rq[p][i][c] = residual code r (see mq_select_blocks) of row (row_block*bn + i),
  *                 column (col_idx[p]*bk + c) for CSR entry p, in CSR order.
- * w: fp32 [N][K]; row_ptr/col_idx as produced by mq_select_blocks (nnz entries);
- * wq: u8 [N][K/2], sw: u16 [N][K/group], rq: u8 [nnz][bn][bk/2] (may be NULL if nnz == 0).
+ * w: fp32 [N][K] row-major; row_ptr/col_idx as produced by mq_select_blocks (nnz
+ * entries); wq, sw, rq in the packed layouts above (rq may be NULL if nnz == 0).
  * Entries with a column-block index outside [0, K/bk) are skipped.
  */
 int mq_pack_weights(const float* w, int64_t N, int64_t K, int group, int bn, int bk,
@@ -115,18 +130,27 @@ int mq_pack_weights(const float* w, int64_t N, int64_t K, int group, int bn, int
  *   y[m][n]    = sx[m] * sum_g ( groups with a chosen block in this row: s_r * T,
  *                                otherwise s * P )            (fp32; s_r = fp32(s/14))
  * which equals sx * sum_g (s*P + s_r*Pr) up to fp32 rounding.
- * xq: u8 [M][K/2], sx: fp32 [M], wq: u8 [N][K/2], sw: u16 [N][K/group],
- * row_ptr: int32 [N/bn+1], col_idx: int32 [nnz], rq: u8 [nnz][bn][bk/2] (NULL if nnz == 0),
+ * xq, wq, sw, rq in the packed layouts above (rq NULL if nnz == 0), sx: fp32 [M],
+ * row_ptr: int32 [N/bn+1], col_idx: int32 [nnz],
  * y: [M][N] fp32 or bf16 (y_dtype, bf16 rounded to nearest even).
  * acc_dump: NULL, or int32 [M][N][K/group] receiving T (a debug build of the same
  * kernel; production calls pass NULL). Indices outside the CSR ranges are ignored,
  * so a malformed list gives wrong values, never an out-of-bounds access.
+ * workspace: device scratch of at least mq_gemm_workspace_bytes(M, N, K) bytes, or
+ * NULL: the call then takes a stream-ordered allocation (hipMallocAsync) and
+ * releases it on the same stream. The current kernels need none (the function
+ * returns 0 for every shape), so NULL costs nothing. A workspace smaller than
+ * required returns MQ_ERR_INVALID_ARG. Calls sharing one workspace must be
+ * ordered on one stream.
  */
 int mq_gemm_w4a4_residual(const uint8_t* xq, const float* sx, const uint8_t* wq,
                           const uint16_t* sw, const int32_t* row_ptr, const int32_t* col_idx,
                           const uint8_t* rq, int64_t nnz, int64_t M, int64_t N, int64_t K,
                           int group, int bn, int bk, void* y, int y_dtype, int32_t* acc_dump,
-                          void* stream);
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes the GEMM calls below need for this shape (0: none). */
+size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
  * Dense-only 4-bit GEMM: the same kernel with the residual path compiled out
@@ -136,7 +160,7 @@ int mq_gemm_w4a4_residual(const uint8_t* xq, const float* sx, const uint8_t* wq,
  */
 int mq_gemm_w4a4_dense(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint16_t* sw,
                        int64_t M, int64_t N, int64_t K, int group, void* y, int y_dtype,
-                       int32_t* acc_dump, void* stream);
+                       int32_t* acc_dump, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The separate-kernel alternative that Methodology 3 argues against: the dense
@@ -150,7 +174,7 @@ int mq_gemm_residual_separate(const uint8_t* xq, const float* sx, const uint8_t*
                               const uint16_t* sw, const int32_t* row_ptr, const int32_t* col_idx,
                               const uint8_t* rq, int64_t nnz, int64_t M, int64_t N, int64_t K,
                               int group, int bn, int bk, void* y, int y_dtype, float* ws,
-                              void* stream);
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

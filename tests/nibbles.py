@@ -2,7 +2,10 @@
 
 Written independently of both the oracle's C code and the HIP library, so a
 mistake in either one's nibble order or sign handling shows up as a mismatch.
-Format: two's-complement int4, low nibble holds the even index, row-major.
+Format: two's-complement int4, low nibble holds the even index. The oracle
+returns row-major arrays; the library's packed layouts (described in
+include/mq.h) are converted back to row-major here with reshapes and transposes
+only, so the comparison is element by element.
 """
 import numpy as np
 
@@ -47,3 +50,26 @@ def rel_err(y, y_ref) -> float:
     den = np.maximum(np.abs(ref), 0.1 * rms)
     den = np.where(den == 0, 1.0, den)
     return float(np.max(np.abs(y - ref) / den)) if y.size else 0.0
+
+
+# ---- the library's packed layouts -> row-major -----------------------------
+def xq_to_rowmajor(dev: np.ndarray, M: int, K: int) -> np.ndarray:
+    """group-major [K/128][M][64] bytes -> [M][K/2]"""
+    a = np.asarray(dev, np.uint8).reshape(K // 128, M, 64)
+    return a.transpose(1, 0, 2).reshape(M, K // 2)
+
+
+def wq_to_rowmajor(dev: np.ndarray, N: int, K: int) -> np.ndarray:
+    """tiles [N/16][G][kc 4][row 16][16 B] -> [N][K/2]"""
+    G = K // 128
+    a = np.asarray(dev, np.uint8).reshape(N // 16, G, 4, 16, 16)
+    return a.transpose(0, 3, 1, 2, 4).reshape(N, K // 2)
+
+
+def sw_to_rowmajor(dev: np.ndarray, N: int, K: int):
+    """[N/16][G4][row 16][4] u16 -> ([N][G] scales, [N][4*G4 - G] padding slots)"""
+    G = K // 128
+    G4 = (G + 3) // 4
+    a = np.asarray(dev).view(np.uint16).reshape(N // 16, G4, 16, 4)
+    full = a.transpose(0, 2, 1, 3).reshape(N, 4 * G4)
+    return full[:, :G], full[:, G:]

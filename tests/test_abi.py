@@ -19,9 +19,14 @@ def _declared():
 
 @pytest.fixture(scope="module")
 def mq():
-    from dense_sparse_bit_amd import _build
-    if not os.path.exists(_build.LIB):
-        _build.build()
+    lib = os.path.join(ROOT, "dense_sparse_bit_amd", "libmq.so")
+    if not os.path.exists(lib):
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_mq_build", os.path.join(ROOT, "dense_sparse_bit_amd", "_build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     import dense_sparse_bit_amd
     return dense_sparse_bit_amd
 
@@ -29,6 +34,7 @@ def mq():
 def test_header_declares_the_boundary():
     names = _declared()
     for fn in ["mq_quantize_act", "mq_pack_weights", "mq_select_blocks", "mq_gemm_w4a4_residual",
+               "mq_gemm_workspace_bytes",
                "mq_hessian_diag", "mq_gemm_w4a4_dense", "mq_gemm_residual_separate",
                "mq_status_string", "mq_version"]:
         assert fn in names
@@ -63,7 +69,7 @@ def _gemm(lib, **kw):
     a.update(kw)
     return lib.mq_gemm_w4a4_residual(a["xq"], a["sx"], a["wq"], a["sw"], a["row_ptr"], a["col_idx"],
                                      a["rq"], a["nnz"], a["M"], a["N"], a["K"], a["group"], a["bn"],
-                                     a["bk"], a["y"], a["y_dtype"], a["dump"], a["stream"])
+                                     a["bk"], a["y"], a["y_dtype"], a["dump"], None, 0, a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -72,6 +78,7 @@ def _gemm(lib, **kw):
     (dict(M=-1), -1), (dict(y_dtype=7), -1), (dict(xq=None), -1), (dict(wq=None), -1),
     (dict(sw=None), -1), (dict(row_ptr=None), -1), (dict(col_idx=None), -1), (dict(rq=None), -1),
     (dict(xq=FAKE + 8), -1), (dict(rq=FAKE + 4), -1), (dict(nnz=-1), -1), (dict(nnz=65), -1),
+    (dict(sw=FAKE + 2), -1), (dict(K=65536 + 128), -2),
 ])
 def test_gemm_rejects_bad_arguments(lib_nogpu, kw, status):
     assert _gemm(lib_nogpu, **kw) == status
@@ -96,9 +103,15 @@ def test_preparation_calls_reject_bad_arguments(lib_nogpu):
     assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, 3, FAKE, FAKE, None, None) == -1
     assert lib.mq_pack_weights(FAKE, 512, 512, 128, 64, 64, None, FAKE, 3, FAKE, FAKE, FAKE, None) == -1
     assert lib.mq_pack_weights(FAKE + 4, 512, 512, 128, 64, 64, FAKE, FAKE, 3, FAKE, FAKE, FAKE, None) == -1
-    assert lib.mq_gemm_w4a4_dense(FAKE, FAKE, FAKE, FAKE, 4, 512, 320, 128, FAKE, 0, None, None) == -2
+    assert lib.mq_gemm_w4a4_dense(FAKE, FAKE, FAKE, FAKE, 4, 512, 320, 128, FAKE, 0, None, None, 0,
+                                  None) == -2
     assert lib.mq_gemm_residual_separate(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 4, 512, 512,
-                                         128, 64, 64, FAKE, 0, None, None) == -1
+                                         128, 64, 64, FAKE, 0, None, None, 0, None) == -1
+    # the packed activation layout is group-major, so K must be a multiple of 128
+    assert lib.mq_quantize_act(FAKE, 1, 4, 130, FAKE, FAKE, None) == -2
+    # the current GEMM kernels need no workspace for any supported shape
+    for M, N, K in [(1, 64, 128), (16, 4096, 4096), (32, 5120, 25600), (2048, 17408, 5120)]:
+        assert lib.mq_gemm_workspace_bytes(M, N, K) == 0
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
@@ -109,6 +122,9 @@ def test_binding_fails_loudly_without_library(tmp_path):
     dst = tmp_path / "dense_sparse_bit_amd"
     dst.mkdir()
     (dst / "__init__.py").write_text(open(os.path.join(pkg, "__init__.py")).read())
+    # and the build script still runs there (it does not import the package)
+    import shutil
+    shutil.copy(os.path.join(pkg, "_build.py"), dst / "_build.py")
     r = subprocess.run([sys.executable, "-c", "import dense_sparse_bit_amd"], cwd=str(tmp_path),
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0 and "libmq.so is missing" in r.stderr

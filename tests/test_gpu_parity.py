@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import synth
-from tests.nibbles import f16_bits_to_f32, rel_err
+from tests.nibbles import rel_err, sw_to_rowmajor, wq_to_rowmajor, xq_to_rowmajor
 
 pytestmark = pytest.mark.gpu
 
@@ -126,10 +126,12 @@ def _check(mq, orc, inp, k_blocks, out_dtype_name="bf16", rows=None, check_varia
     np.testing.assert_array_equal(_np(g["delta"]), pre["delta"])
     np.testing.assert_array_equal(_np(g["row_ptr"]), ref["row_ptr"])
     np.testing.assert_array_equal(_np(g["col_idx"]), ref["col_idx"])
-    np.testing.assert_array_equal(_np(g["wq"]), ref["wq"])
-    np.testing.assert_array_equal(_np(g["sw"]).view(np.uint16), ref["sw"])
+    np.testing.assert_array_equal(wq_to_rowmajor(_np(g["wq"]), cfg.N, cfg.K), ref["wq"])
+    sw, pad = sw_to_rowmajor(_np(g["sw"]), cfg.N, cfg.K)
+    np.testing.assert_array_equal(sw, ref["sw"])
+    assert not pad.any(), "padding slots of sw must be zero"
     np.testing.assert_array_equal(_np(g["rq"]), ref["rq"])
-    np.testing.assert_array_equal(_np(g["xq"]), pre["xq"])
+    np.testing.assert_array_equal(xq_to_rowmajor(_np(g["xq"]), cfg.M, cfg.K), pre["xq"])
     np.testing.assert_array_equal(_np(g["sx"]), pre["sx"])
     sel = slice(None) if rows is None else rows
     dump = g["dump"][sel] if rows is None else g["dump"][torch.as_tensor(rows, device="cuda")]
@@ -230,10 +232,10 @@ def test_degenerate_rows_and_groups(mq, orc):
 
 def test_zero_tokens_no_op(mq):
     import torch
-    xq = torch.empty((0, 256), dtype=torch.uint8, device="cuda")
+    xq = torch.empty((4, 0, 64), dtype=torch.uint8, device="cuda")
     sx = torch.empty(0, dtype=torch.float32, device="cuda")
-    wq = torch.zeros((128, 256), dtype=torch.uint8, device="cuda")
-    sw = torch.zeros((128, 4), dtype=torch.int16, device="cuda")
+    wq = torch.zeros((8, 4, 1024), dtype=torch.uint8, device="cuda")
+    sw = torch.zeros((8, 1, 16, 4), dtype=torch.int16, device="cuda")
     rp = torch.zeros(3, dtype=torch.int32, device="cuda")
     none = torch.empty(0, dtype=torch.int32, device="cuda")
     y = mq.gemm_w4a4_residual(xq, sx, wq, sw, rp, none, none, 512, bn=64)
