@@ -73,12 +73,12 @@ struct DecStep {
     int rg;            // bit u: group 4q+u holds a chosen block in this block row
 };
 
-template <int MT, bool RES>
-__device__ __forceinline__ void dec_fetch(DecStep<MT>& st, const GemmArgs& a, const int* tab, int nt, int rrow,
-                                          int G, int G4, int q, int lane) {
+// base tiles, activations and scales of quad q
+template <int MT>
+__device__ __forceinline__ void dec_fetch_main(DecStep<MT>& st, const GemmArgs& a, int nt, int G, int G4, int q,
+                                               int lane) {
     const int li = lane & 15, kg = lane >> 4;
     const uint4 z = make_uint4(0, 0, 0, 0);
-    st.rg = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int g = 4 * q + u;
@@ -89,15 +89,28 @@ __device__ __forceinline__ void dec_fetch(DecStep<MT>& st, const GemmArgs& a, co
             const int m = t * 16 + li;
             st.x[t][u] = ok && m < a.M ? ldg16(a.xq + xq_row(g, a.M, m) + kg * 16) : z;
         }
-        st.r[u] = z;
-        if (RES && ok) {
+    }
+    st.s = *reinterpret_cast<const uint2*>(a.sw + ((static_cast<int64_t>(nt) * G4 + q) * 16 + li) * 4);
+}
+
+// residual rows of quad q: the zipper table gives each column block's CSR
+// position (or -1); lanes 0-31 take the group's first block, 32-63 the second
+template <int MT, bool RES>
+__device__ __forceinline__ void dec_fetch_res(DecStep<MT>& st, const GemmArgs& a, const int* tab, int rrow, int G,
+                                              int q, int lane) {
+    const int kg = lane >> 4;
+    st.rg = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int g = 4 * q + u;
+        st.r[u] = make_uint4(0, 0, 0, 0);
+        if (RES && g < G) {
             const int j0 = tab[2 * g], j1 = tab[2 * g + 1];
             if (j0 >= 0 || j1 >= 0) st.rg |= 1 << u;
             const int j = kg < 2 ? j0 : j1;
             if (j >= 0) st.r[u] = ldg16(a.rq + (static_cast<int64_t>(j) * a.bn + rrow) * 32 + (kg & 1) * 16);
         }
     }
-    st.s = *reinterpret_cast<const uint2*>(a.sw + ((static_cast<int64_t>(nt) * G4 + q) * 16 + li) * 4);
 }
 
 template <int MT, bool RES, bool DUMP>
@@ -146,18 +159,12 @@ __device__ __forceinline__ void dec_compute(const DecStep<MT>& st, const GemmArg
 template <int MT, bool RES, bool DUMP, int OUTMODE>
 __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a) {
     __shared__ float red[kMaxDecodeWaves * MT * 256];
-    __shared__ int tab[RES ? 2 * kMaxGroups : 1];
+    __shared__ int tab[RES ? 8 * (kMaxGroups / 4) : 1];   // column block -> CSR position
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int G = a.K / kGroup, G4 = (G + 3) / 4;
     const int nt = blockIdx.x, n0 = nt * 16, n = n0 + (lane & 15);
     const int br = n0 / a.bn, rrow = n - br * a.bn;
     const int q0 = wave * G4 / nw, q1 = (wave + 1) * G4 / nw;
-    if (RES) {
-        for (int i = tid; i < 2 * G; i += blockDim.x) tab[i] = -1;
-        __syncthreads();
-        zip_table(a, br, 0, 2 * G, tab, tid, blockDim.x);
-        __syncthreads();
-    }
     float acc[MT][4];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
@@ -167,12 +174,35 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
     // two quads in flight: quad q+1 is fetched while q is multiplied (ping-pong
     // buffers, so no register copy waits on the prefetch)
     DecStep<MT> s0, s1;
-    if (q0 < q1) dec_fetch<MT, RES>(s0, a, tab, nt, rrow, G, G4, q0, lane);
+    if (q0 < q1) dec_fetch_main<MT>(s0, a, nt, G, G4, q0, lane);
+    if (RES) {
+        // The zipper table of this wave's column blocks [8 q0, 8 q1), built by the
+        // wave alone while its first loads are in flight: no workgroup barrier.
+        // A wavefront's LDS operations complete in issue order, so the -1 fill,
+        // the CSR positions and the later reads need no wait between lanes.
+        const int kb0 = 8 * q0, kb1 = min(8 * q1, 2 * G);
+        for (int i = kb0 + lane; i < kb1; i += 64) tab[i] = -1;
+        __builtin_amdgcn_wave_barrier();
+        const int lo = clampi(a.row_ptr[br], 0, a.nnz);
+        const int hi = clampi(a.row_ptr[br + 1], lo, a.nnz);
+        for (int i = lo + lane; i < hi; i += 64) {
+            const int kb = a.col_idx[i];
+            if (kb >= kb0 && kb < kb1) tab[kb] = i;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (q0 < q1) dec_fetch_res<MT, RES>(s0, a, tab, rrow, G, q0, lane);
+    }
     for (int q = q0; q < q1; q += 2) {
-        if (q + 1 < q1) dec_fetch<MT, RES>(s1, a, tab, nt, rrow, G, G4, q + 1, lane);
+        if (q + 1 < q1) {
+            dec_fetch_main<MT>(s1, a, nt, G, G4, q + 1, lane);
+            if (RES) dec_fetch_res<MT, RES>(s1, a, tab, rrow, G, q + 1, lane);
+        }
         dec_compute<MT, RES, DUMP>(s0, a, n, G, q, lane, acc);
         if (q + 1 >= q1) break;
-        if (q + 2 < q1) dec_fetch<MT, RES>(s0, a, tab, nt, rrow, G, G4, q + 2, lane);
+        if (q + 2 < q1) {
+            dec_fetch_main<MT>(s0, a, nt, G, G4, q + 2, lane);
+            if (RES) dec_fetch_res<MT, RES>(s0, a, tab, rrow, G, q + 2, lane);
+        }
         dec_compute<MT, RES, DUMP>(s1, a, n, G, q + 1, lane, acc);
     }
 
@@ -202,7 +232,7 @@ constexpr int kRowB = 80;          // LDS bytes per tile row: 64 data + 16 pad (
 constexpr int kMaxKb = 1024;       // column blocks per row the LDS zipper table holds (K <= 65536)
 
 template <bool RES, bool DUMP, int OUTMODE>
-__global__ __launch_bounds__(256) void k_gemm_tiled(GemmArgs a) {
+__global__ __launch_bounds__(256, (RES || DUMP) ? 1 : 2) void k_gemm_tiled(GemmArgs a) {
     __shared__ __align__(16) uint8_t As[2][kBM * kRowB];
     __shared__ __align__(16) uint8_t Bs[2][kBN * kRowB];
     __shared__ int jtab[RES ? 2 * kMaxKb : 1];

@@ -96,6 +96,34 @@ __device__ __forceinline__ Elem quant_elem(float w, const GroupScale& g) {
     return o;
 }
 
+// Branch-free form of rtn_codef for long runs of elements. Returns the code of
+// rint(v * rs) clamped to [-7, 7] and raises `worst` to |t - rint(t)|. While the
+// caller's worst stays below 0.5 - 4e-6 (and rs is finite), every code equals
+// rtn_codef's: no half-integer lies between t and fl(v/s) when |t| <= 8, and for
+// larger |t| both quotients clamp to the same +-7. Otherwise the caller redoes the
+// run with rtn_codef. s == 0 needs no special case: rs = 0 gives t = 0, code 0.
+__device__ __forceinline__ float rtn_fast(float v, float rs, float& worst) {
+    const float t = v * rs;
+    const float q = __builtin_rintf(t);
+    worst = fmaxf(worst, fabsf(t - q));
+    return fminf(fmaxf(q, -7.0f), 7.0f);
+}
+constexpr float kFastMargin = 0.5f - 4e-6f;
+
+// quant_elem through rtn_fast (valid when the run's worst stays below kFastMargin)
+__device__ __forceinline__ Elem quant_elem_fast(float w, const GroupScale& g, float& worst) {
+    Elem o;
+    o.q = rtn_fast(w, g.rs, worst);
+    o.e = __builtin_fmaf(-g.s, o.q, w);
+    o.r = rtn_fast(o.e, g.rsr, worst);
+    o.ep = __builtin_fmaf(-g.sr, o.r, o.e);
+    return o;
+}
+// the reciprocals are finite, so rtn_fast's t is finite for finite inputs
+__device__ __forceinline__ bool fast_ok(const GroupScale& g) {
+    return fabsf(g.rs) <= 3.0e38f && fabsf(g.rsr) <= 3.0e38f;
+}
+
 // ---- int4 -> int8 operand construction for the int8 MFMA ------------------
 // A 32-bit word holds 8 two's-complement nibbles (k0 in bits 0-3). Placing a
 // nibble in the high half of a byte gives the int8 value 16*v, so two masks

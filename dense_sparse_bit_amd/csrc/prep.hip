@@ -13,10 +13,16 @@
 // This file is compiled with -ffp-contract=off: every fp32/fp64 operation is
 // rounded on its own, in the order written, so codes, scales and scores are
 // bit-identical to the plain CPU definition.
+#include <algorithm>
+
 #include "mq_device.h"
 #include "mq_internal.h"
 
 namespace mq {
+
+// native 4-float vector (HIP's float4 is a union struct, which keeps a
+// loop-carried array of them in scratch memory)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // a0: h_k = fp32( sum_{m ascending} x_mk^2 / M ). A workgroup owns 64 channels:
@@ -79,6 +85,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, i
                            : static_cast<const void*>(static_cast<const float*>(x) + m * K);
     const int t = threadIdx.x;
     __shared__ float red[4];
+    __shared__ uint8_t fixb[4][kQaRegs];       // per-wave code bytes of a repaired lane
     float2 v[kQaRegs];
     float a = 0.0f;
 #pragma unroll
@@ -101,10 +108,51 @@ __global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, i
     // group-major output: byte j of the row (inputs 2j, 2j+1) goes to group j/64
     auto code = [&](float v) { return static_cast<int>(rtn_codef(v, s, rs)) & 15; };
     auto dst = [&](int64_t j) { return xq + xq_row(j >> 6, M, m) + (j & 63); };
+    // branch-free codes for the values held in registers; rare near-ties (or a
+    // non-finite reciprocal) redo them with the exact quantizer
+    static_assert(kQaRegs == 16, "four code bytes per word, four words");
+    uint32_t wd[4] = {0, 0, 0, 0};
+    float worst = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kQaRegs; ++i) {
+        const uint32_t c = (static_cast<uint32_t>(static_cast<int>(rtn_fast(v[i].x, rs, worst))) & 15u) |
+                           ((static_cast<uint32_t>(static_cast<int>(rtn_fast(v[i].y, rs, worst))) & 15u) << 4);
+        wd[i >> 2] |= c << (8 * (i & 3));
+    }
+    uint4 bytes = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    const bool redo = !(worst < kFastMargin) || !(fabsf(rs) <= 3.0e38f);
+    // Rare: a quotient within 4e-6 of a rounding boundary. The wave repairs each
+    // flagged lane L together: lane i < 16 recodes L's pair i exactly, and L
+    // gathers the bytes through LDS.
+    uint64_t flagged = __ballot(redo);
+    while (flagged) {
+        const int L = __builtin_ctzll(flagged);
+        flagged &= flagged - 1;
+        const int tL = (t & ~63) + L;
+        if ((t & 63) < kQaRegs) {
+            const int64_t j = tL + 256 * (t & 63);
+            uint8_t c = 0;
+            if (j < P) {
+                const float2 u = load_pair(row, bf16, j);
+                c = static_cast<uint8_t>((static_cast<int>(rtn_codef(u.x, s, rs)) & 15) |
+                                         ((static_cast<int>(rtn_codef(u.y, s, rs)) & 15) << 4));
+            }
+            fixb[t >> 6][t & 63] = c;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if ((t & 63) == L) {
+            uint32_t f[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < kQaRegs; ++i) f[i >> 2] |= static_cast<uint32_t>(fixb[t >> 6][i]) << (8 * (i & 3));
+            bytes = make_uint4(f[0], f[1], f[2], f[3]);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    const uint32_t bw[4] = {bytes.x, bytes.y, bytes.z, bytes.w};
 #pragma unroll
     for (int i = 0; i < kQaRegs; ++i) {
         const int64_t j = t + 256 * i;
-        if (j < P) *dst(j) = static_cast<uint8_t>(code(v[i].x) | (code(v[i].y) << 4));
+        if (j < P) *dst(j) = static_cast<uint8_t>(bw[i >> 2] >> (8 * (i & 3)));
     }
     for (int64_t j = t + 256 * kQaRegs; j < P; j += 256) {
         const float2 u = load_pair(row, bf16, j);
@@ -113,66 +161,173 @@ __global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, i
 }
 
 // ---------------------------------------------------------------------------
-// a2 (part 1): Delta-score. One workgroup per (block row, two groups); a lane
-// owns one (group, row, block) chain: it loads the row's 64 weights of that block
-// (sixteen 16-byte loads, all in flight together), takes the group max with its
-// partner lane (exact), and adds its 64 terms h_k * (E^2 - E'^2) strictly in
-// column order. Block score = sum over the block's rows in ascending order.
+// a2 (part 1): Delta-score. A workgroup of two waves owns one group g and walks
+// a strided set of block rows (about four workgroups per CU in total); each
+// wave owns 32 rows of a block row per pass, and lane l runs the chain of row
+// l % 32, column block l / 32 (64 terms h_k * (E^2 - E'^2) strictly in column
+// order) after taking the group max with its partner lane (exact).
+// The chains need 64 consecutive floats per lane, which direct loads would fetch
+// as 64 scattered 16-byte pieces per wave instruction; instead the wave loads its
+// 32 x 128 fp32 slab with 1 KB-contiguous instructions (two rows' group chunks)
+// and stages it in LDS, swizzled (16-byte slot c of row r at c ^ (r & 7)) so that
+// both the stores and the per-lane 16-byte reads are free of bank conflicts. The
+// next pass's slab is loaded into registers while the current one is computed.
+// A wave only reads rows it wrote itself and its LDS operations complete in issue
+// order, so only the per-block row sum needs a workgroup barrier. Block score =
+// sum of the block's row chains in ascending row order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_delta(const float* __restrict__ w, const float* __restrict__ h,
-                                               int64_t K, int bn, double* __restrict__ delta,
+constexpr int kDeltaRows = 32;                 // rows per wave and pass
+
+// (double)E^2 - (double)E'^2 of 8 elements through rtn_fast, computed stage by
+// stage: every stage is 8 independent operations.
+__device__ __forceinline__ void quant_reduction8(const float (&w)[8], const GroupScale& g, float& worst,
+                                                 double (&red)[8]) {
+    float t[8], q[8], e[8], r[8], ep[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = w[i] * g.rs;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = __builtin_rintf(t[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) worst = fmaxf(worst, fabsf(t[i] - q[i]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = __builtin_fmaf(-g.s, fminf(fmaxf(q[i], -7.0f), 7.0f), w[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t[i] = e[i] * g.rsr;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = __builtin_rintf(t[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) worst = fmaxf(worst, fabsf(t[i] - r[i]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ep[i] = __builtin_fmaf(-g.sr, fminf(fmaxf(r[i], -7.0f), 7.0f), e[i]);
+    double de[8], dp[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) de[i] = static_cast<double>(e[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dp[i] = static_cast<double>(ep[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) de[i] = de[i] * de[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dp[i] = dp[i] * dp[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[i] = de[i] - dp[i];
+}
+
+__device__ __forceinline__ void delta_load(f32x4 (&v)[kDeltaRows / 2], const float* __restrict__ w, int64_t K,
+                                           int64_t row0, int64_t g, int lane) {
+#pragma unroll
+    for (int i = 0; i < kDeltaRows / 2; ++i) {
+        const int r = 2 * i + (lane >> 5);
+        v[i] = *reinterpret_cast<const f32x4*>(w + (row0 + r) * K + g * kGroup + (lane & 31) * 4);
+    }
+}
+
+// LDS allows four workgroups (8 waves) per CU, so 2 waves per SIMD is the real
+// occupancy; the attribute lets the prefetched slab stay in registers
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void k_delta(const float* __restrict__ w, const float* __restrict__ h,
+                                               int64_t K, int bn, int nbr, double* __restrict__ delta,
                                                int32_t* __restrict__ rank) {
-    __shared__ float hs[2][kGroup];
-    __shared__ double rowsum[2][2][128];
-    const int64_t G = K / kGroup, nbc = K / kBk;
-    const int t = threadIdx.x, gsel = t >> 7, row = (t & 127) >> 1, half = t & 1;
-    const int64_t br = blockIdx.x, g = 2 * static_cast<int64_t>(blockIdx.y) + gsel;
-    const bool valid = g < G;                        // uniform per wavefront
-    hs[gsel][t & 127] = valid ? h[g * kGroup + (t & 127)] : 0.0f;
+    __shared__ __align__(16) f32x4 slab[2][kDeltaRows][32];    // [wave][row][16-byte slot]
+    __shared__ double hs[kGroup];
+    __shared__ double rowsum[2][128];                          // [column block][row of the block]
+    __shared__ double fixbuf[2][kBk];                          // per-wave terms of a repaired chain
+    const int64_t nbc = K / kBk;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int64_t g = blockIdx.y;
+    const int P = gridDim.x, br0 = blockIdx.x;
+    hs[t] = static_cast<double>(h[g * kGroup + t]);
     __syncthreads();
-    const float* hrow = hs[gsel] + half * kBk;
-    for (int r0 = 0; r0 < bn; r0 += 64) {
-        if (valid) {
-            const float* src = w + (br * bn + r0 + row) * K + g * kGroup + half * kBk;
-            float wv[kBk];
+    const int crow = lane & 31, half = lane >> 5;              // this lane's chain
+    const double* hrow = hs + half * kBk;
+    f32x4 (*mine)[32] = slab[wv];
+    const int ppu = bn / (2 * kDeltaRows);                     // passes per block row
+    const int units = br0 < nbr ? (nbr - br0 + P - 1) / P : 0;
+    const int passes = units * ppu;
+    // first row of this wave's 32 rows in pass ps
+#define MQ_PASS_ROW0(ps) \
+    ((br0 + static_cast<int64_t>((ps) / ppu) * P) * bn + ((ps) % ppu) * (2 * kDeltaRows) + wv * kDeltaRows)
+    f32x4 v[kDeltaRows / 2];
+    if (passes > 0) delta_load(v, w, K, MQ_PASS_ROW0(0), g, lane);
+    for (int ps = 0; ps < passes; ++ps) {
 #pragma unroll
-            for (int i = 0; i < kBk / 4; ++i) {
-                const float4 u = *reinterpret_cast<const float4*>(src + 4 * i);
-                wv[4 * i] = u.x; wv[4 * i + 1] = u.y; wv[4 * i + 2] = u.z; wv[4 * i + 3] = u.w;
+        for (int i = 0; i < kDeltaRows / 2; ++i) {
+            const int r = 2 * i + (lane >> 5);
+            mine[r][(lane & 31) ^ (r & 7)] = v[i];
+        }
+        __builtin_amdgcn_wave_barrier();
+        // next pass's slab in flight meanwhile (the last pass reloads its own rows)
+        const int nxt = ps + 1 < passes ? ps + 1 : ps;
+        delta_load(v, w, K, MQ_PASS_ROW0(nxt), g, lane);
+        // two passes over the row in LDS: the group max, then the chain in chunks
+        // of 8 values (keeps the registers for the prefetched slab free)
+        float a = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kBk / 4; ++j) {
+            const f32x4 u = mine[crow][(half * 16 + j) ^ (crow & 7)];
+            a = fmaxf(a, fmaxf(fmaxf(fabsf(u.x), fabsf(u.y)), fmaxf(fabsf(u.z), fabsf(u.w))));
+        }
+        a = fmaxf(a, __shfl_xor(a, 32));
+        const GroupScale gs = group_scale(f16_bits_to_f32(f32_to_f16_bits(a / 7.0f)));
+        // branch-free chain; a lane whose quotients came within 4e-6 of a rounding
+        // boundary (rare) redoes it with the exact quantizer afterwards
+        double acc = 0.0;
+        float worst = 0.0f;
+#pragma unroll
+        for (int i0 = 0; i0 < kBk; i0 += 8) {
+            // bounded scheduling window: keeps the live range of the per-element
+            // temporaries short (no spills)
+            __builtin_amdgcn_sched_barrier(0);
+            const f32x4 u0 = mine[crow][(half * 16 + i0 / 4) ^ (crow & 7)];
+            const f32x4 u1 = mine[crow][(half * 16 + i0 / 4 + 1) ^ (crow & 7)];
+            const float wc[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+            // stage by stage over the 8 elements, so their independent work
+            // interleaves (one element at a time is a single dependency chain)
+            double red[8];
+            quant_reduction8(wc, gs, worst, red);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc = acc + hrow[i0 + i] * red[i];
+        }
+        const bool redo = !(worst < kFastMargin) || !fast_ok(gs);
+        // Rare repair, done by the whole wave: for each flagged chain (lane L) every
+        // lane requantizes one of its 64 elements exactly, and lane L adds the 64
+        // terms in column order. Same operations and order as the chain itself,
+        // so the result is bit-identical; a lane redoing its own chain serially
+        // would put ~20k dependent cycles on the workgroup's critical path.
+        uint64_t flagged = __ballot(redo);
+        while (flagged) {
+            const int L = __builtin_ctzll(flagged);
+            flagged &= flagged - 1;
+            const int lrow = L & 31, lhalf = L >> 5;
+            const float ls = __shfl(gs.s, L);
+            const GroupScale lg = group_scale(ls);
+            const f32x4 u = mine[lrow][(lhalf * 16 + (lane >> 2)) ^ (lrow & 7)];
+            const float x = (lane & 3) == 0 ? u.x : (lane & 3) == 1 ? u.y : (lane & 3) == 2 ? u.z : u.w;
+            const Elem o = quant_elem(x, lg);
+            const double e = o.e, ep = o.ep;
+            fixbuf[wv][lane] = hs[lhalf * kBk + lane] * (e * e - ep * ep);
+            __builtin_amdgcn_wave_barrier();
+            if (lane == L) {
+                double a2 = 0.0;
+                for (int i = 0; i < kBk; ++i) a2 = a2 + fixbuf[wv][i];
+                acc = a2;
             }
-            float a = 0.0f;
-#pragma unroll
-            for (int i = 0; i < kBk; ++i) a = fmaxf(a, fabsf(wv[i]));
-            a = fmaxf(a, __shfl_xor(a, 1));
-            const GroupScale gs = group_scale(f16_bits_to_f32(f32_to_f16_bits(a / 7.0f)));
-            double acc = 0.0;
-#pragma unroll
-            for (int i0 = 0; i0 < kBk; i0 += 8) {
-                // bounded scheduling window: keeps the live range of the
-                // per-element temporaries short (no spills)
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int i = i0; i < i0 + 8; ++i) {
-                    const Elem o = quant_elem(wv[i], gs);
-                    const double e = o.e, ep = o.ep;
-                    const double reduction = e * e - ep * ep;
-                    acc = acc + static_cast<double>(hrow[i]) * reduction;
-                }
+            __builtin_amdgcn_wave_barrier();
+        }
+        __builtin_amdgcn_wave_barrier();
+        rowsum[half][(ps % ppu) * (2 * kDeltaRows) + wv * kDeltaRows + crow] = acc;
+        if ((ps + 1) % ppu == 0) {
+            __syncthreads();
+            if (t < 2) {
+                const int64_t br = br0 + static_cast<int64_t>(ps / ppu) * P;
+                double total = 0.0;
+                for (int r = 0; r < bn; ++r) total = total + rowsum[t][r];
+                delta[br * nbc + 2 * g + t] = total;
+                rank[br * nbc + 2 * g + t] = 0;     // counters for the ranking pass
             }
-            rowsum[gsel][half][r0 + row] = acc;
+            __syncthreads();
         }
     }
-    __syncthreads();
-    if (t < 4) {
-        const int gs2 = t >> 1, hf = t & 1;
-        const int64_t gg = 2 * static_cast<int64_t>(blockIdx.y) + gs2;
-        if (gg < G) {
-            double total = 0.0;
-            for (int r = 0; r < bn; ++r) total = total + rowsum[gs2][hf][r];
-            delta[br * nbc + 2 * gg + hf] = total;
-            rank[br * nbc + 2 * gg + hf] = 0;     // counters for the ranking pass
-        }
-    }
+#undef MQ_PASS_ROW0
 }
 
 // ---------------------------------------------------------------------------
@@ -267,6 +422,7 @@ __global__ __launch_bounds__(1024) void k_csr(const int32_t* __restrict__ rank, 
 // parallel, for the two column blocks of the group; chosen blocks get their
 // 16-byte residual rows written at their CSR position. W is read exactly once.
 // ---------------------------------------------------------------------------
+
 __device__ __forceinline__ uint32_t pack8(const int* c) {
     uint32_t v = 0;
 #pragma unroll
@@ -280,8 +436,9 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64
                                               uint8_t* __restrict__ wq, uint16_t* __restrict__ sw,
                                               uint8_t* __restrict__ rq) {
     __shared__ int pos[2];
+    __shared__ uint8_t fix[4][64];                 // per-wave codes of a repaired lane
     const int64_t br = blockIdx.x, g = blockIdx.y, G = K / kGroup, G4 = (G + 3) / 4;
-    const int t = threadIdx.x, row = t >> 2, qd = t & 3;
+    const int t = threadIdx.x, row = t >> 2, qd = t & 3, lane = t & 63, wave = t >> 6;
     // first 64 rows' weights are requested before the list search, so the two
     // latencies overlap
     float wv0[32];
@@ -328,23 +485,53 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64
         const uint16_t sb = f32_to_f16_bits(a / 7.0f);
         const GroupScale gs = group_scale(f16_bits_to_f32(sb));
         int qc[32], rc[32];
+        float worst = 0.0f;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-            const Elem o = quant_elem(wv[i], gs);
+            const Elem o = quant_elem_fast(wv[i], gs, worst);
             qc[i] = static_cast<int>(o.q);
             rc[i] = static_cast<int>(o.r);
         }
+        uint4 cq = make_uint4(pack8(qc), pack8(qc + 8), pack8(qc + 16), pack8(qc + 24));
+        uint4 cr = make_uint4(pack8(rc), pack8(rc + 8), pack8(rc + 16), pack8(rc + 24));
+        // Rare: a quotient within 4e-6 of a rounding boundary. The wave repairs each
+        // flagged lane L together: lane i < 32 requantizes weight i of L's 32 with
+        // the exact quantizer, and L gathers the codes through LDS.
+        const bool redo = !(worst < kFastMargin) || !fast_ok(gs);
+        uint64_t flagged = __ballot(redo);
+        while (flagged) {
+            const int L = __builtin_ctzll(flagged);
+            flagged &= flagged - 1;
+            const int64_t nL = __shfl(static_cast<int>(n), L);
+            const int qdL = L & 3;
+            const GroupScale lg = group_scale(__shfl(gs.s, L));
+            if (lane < 32) {
+                const Elem o = quant_elem(w[nL * K + g * kGroup + qdL * 32 + lane], lg);
+                fix[wave][lane] = static_cast<uint8_t>(static_cast<int>(o.q) & 15);
+                fix[wave][32 + lane] = static_cast<uint8_t>(static_cast<int>(o.r) & 15);
+            }
+            __builtin_amdgcn_wave_barrier();
+            if (lane == L) {
+                uint32_t q4[4] = {0, 0, 0, 0}, r4[4] = {0, 0, 0, 0};
+#pragma unroll
+                for (int i = 0; i < 32; ++i) {
+                    q4[i >> 3] |= static_cast<uint32_t>(fix[wave][i]) << (4 * (i & 7));
+                    r4[i >> 3] |= static_cast<uint32_t>(fix[wave][32 + i]) << (4 * (i & 7));
+                }
+                cq = make_uint4(q4[0], q4[1], q4[2], q4[3]);
+                cr = make_uint4(r4[0], r4[1], r4[2], r4[3]);
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
         // tiled base codes: a wavefront's 16 rows x 4 quarters are one 1 KB tile
-        *reinterpret_cast<uint4*>(wq + wq_byte(n, G, g, qd)) =
-            make_uint4(pack8(qc), pack8(qc + 8), pack8(qc + 16), pack8(qc + 24));
+        *reinterpret_cast<uint4*>(wq + wq_byte(n, G, g, qd)) = cq;
         if (qd == 0) {
             sw[sw_index(n, G4, g)] = sb;
             if (g == G - 1)
                 for (int64_t gp = G; gp < 4 * G4; ++gp) sw[sw_index(n, G4, gp)] = 0;   // padding slots
         }
         if (p >= 0)
-            *reinterpret_cast<uint4*>(rq + (static_cast<int64_t>(p) * bn + r0 + row) * (kBk / 2) + (qd & 1) * 16) =
-                make_uint4(pack8(rc), pack8(rc + 8), pack8(rc + 16), pack8(rc + 24));
+            *reinterpret_cast<uint4*>(rq + (static_cast<int64_t>(p) * bn + r0 + row) * (kBk / 2) + (qd & 1) * 16) = cr;
     }
 }
 
@@ -370,8 +557,11 @@ hipError_t launch_select(const float* w, const float* h, int64_t N, int64_t K, i
     int32_t* rank = nullptr;
     hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&rank), static_cast<size_t>(nb) * sizeof(int32_t), st);
     if (err != hipSuccess) return err;
-    k_delta<<<dim3(static_cast<unsigned>(nbr), static_cast<unsigned>((K / kGroup + 1) / 2)), dim3(256), 0, st>>>(
-        w, h, K, bn, delta, rank);
+    // about four workgroups per CU: each walks nbr / P block rows of one group
+    const int64_t G = K / kGroup;
+    const int64_t P = std::max<int64_t>(1, std::min<int64_t>(nbr, (1024 + G - 1) / G));
+    k_delta<<<dim3(static_cast<unsigned>(P), static_cast<unsigned>(G)), dim3(128), 0, st>>>(
+        w, h, K, bn, static_cast<int>(nbr), delta, rank);
     err = hipGetLastError();
     const unsigned nblk = static_cast<unsigned>((nb + 255) / 256);
     if (err == hipSuccess) {
