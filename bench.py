@@ -10,8 +10,9 @@ HBM before the timed region; consecutive steps read different copies of them
 (more than 600 MB in total) so the 256 MB Infinity Cache cannot serve them.
 
 Printed on stdout: one JSON line. `value` is the step's algorithmic HBM bytes
-per second; `roofline` is the kernel that takes most of the step, timed with
-HIP events on the launch stream; `gemm` is the fused kernel alone (the metric's
+per second, the step timed as one replay of a HIP graph of `steps` steps;
+`roofline` is the call that takes most of the step, timed alone in its own graph
+with HIP events on the launch stream; `gemm` is the fused kernel alone (the metric's
 TOPS and GB/s), timed over rotated packed-weight copies, beside the dense-only
 kernel and the separate-kernel alternative; `cpu_baseline` is the CPU oracle on
 the host, one core, on the same workload.
@@ -69,7 +70,35 @@ def step_bytes(cfg, nnz, x_bytes):
 
 
 # --------------------------------------------------------------------------- GPU legs
+def _graph_time_us(torch, fn, n_calls, reps=5):
+    """Median per-call time of `n_calls` back-to-back calls of fn(i) captured in one
+    HIP graph (HIP events around each replay, on the capturing stream)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n_calls):
+            fn(i)
+    times = []
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / n_calls)
+    del graph
+    return float(np.median(times[1:]))
+
+
 def bench_step(mq, torch, cfg, inp, k_blocks, steps, warmup):
+    """The whole path, step after step, over rotating input copies. The timed
+    region is one replay of a HIP graph holding exactly `steps` steps (launch
+    overhead of the Python binding excluded); each call is also timed alone."""
     dev = torch.device("cuda:0")
     x_bytes = 2 if inp.X_bits is not None else 4
     per_copy = cfg.N * cfg.K * 4 + cfg.M * cfg.K * x_bytes
@@ -83,66 +112,97 @@ def bench_step(mq, torch, cfg, inp, k_blocks, steps, warmup):
     ws = [w0.clone() for _ in range(copies)]
     del x0, w0
     N, K, M, bn = cfg.N, cfg.K, cfg.M, cfg.bn
+    G = K // 128
     nb = (N // bn) * (K // cfg.bk)
     h = torch.empty(K, dtype=torch.float32, device=dev)
     sel_out = (torch.empty(N // bn + 1, dtype=torch.int32, device=dev),
                torch.empty(max(k_blocks, 1), dtype=torch.int32, device=dev),
                torch.empty(nb, dtype=torch.float64, device=dev))
-    G = K // 128
+    sel_ws = mq.select_workspace(N, K, bn=bn, device=dev)
     pack_out = (torch.empty((N // 16, G, 1024), dtype=torch.uint8, device=dev),
                 torch.empty((N // 16, (G + 3) // 4, 16, 4), dtype=torch.int16, device=dev),
                 torch.empty((max(k_blocks, 1), bn, 32), dtype=torch.uint8, device=dev))
     xq = torch.empty((G, M, 64), dtype=torch.uint8, device=dev)
     sx = torch.empty(M, dtype=torch.float32, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    names = ["hessian_diag", "select_blocks", "pack_weights", "quantize_act", "gemm_w4a4_residual"]
+    gemm_ws = mq.workspace(M, N, K, device=dev)
     log(f"[bench] step workload {cfg.name}: M={M} K={K} N={N} bn={bn} k_blocks={k_blocks}, "
         f"{copies} input copies ({copies * per_copy / 2**20:.0f} MiB)")
 
-    def one_step(i, ev=None):
-        x, w = xs[i % copies], ws[i % copies]
-        if ev is not None:
-            ev[0].record()
-        mq.hessian_diag(x, out=h)
-        if ev is not None:
-            ev[1].record()
-        rp, ci, _ = mq.select_blocks(w, h, k_blocks, bn=bn, out=sel_out)
-        if ev is not None:
-            ev[2].record()
-        wq, sw, rq = mq.pack_weights(w, rp, ci, bn=bn, out=pack_out)
-        if ev is not None:
-            ev[3].record()
-        mq.quantize_act(x, xq=xq, sx=sx)
-        if ev is not None:
-            ev[4].record()
-        mq.gemm_w4a4_residual(xq, sx, wq, sw, rp, ci, rq, K, bn=bn, y=y)
-        if ev is not None:
-            ev[5].record()
+    def hess(i):
+        mq.hessian_diag(xs[i % copies], out=h)
+
+    def select(i):
+        return mq.select_blocks(ws[i % copies], h, k_blocks, bn=bn, out=sel_out, workspace=sel_ws)
+
+    def pack(i):
+        rp, ci = sel_out[0], sel_out[1][:k_blocks]
+        return mq.pack_weights(ws[i % copies], rp, ci, bn=bn, out=pack_out)
+
+    def quant(i):
+        mq.quantize_act(xs[i % copies], xq=xq, sx=sx)
+
+    def gemm(i):
+        wq, sw, rq = pack_out[0], pack_out[1], pack_out[2][:k_blocks]
+        mq.gemm_w4a4_residual(xq, sx, wq, sw, sel_out[0], sel_out[1][:k_blocks], rq, K, bn=bn, y=y,
+                              workspace=gemm_ws)
+
+    def one_step(i):
+        hess(i)
+        select(i)
+        pack(i)
+        quant(i)
+        gemm(i)
 
     for i in range(warmup):
         one_step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
-    torch.cuda.synchronize()
+    # eager steps (Python launch path included), for reference
     t0 = time.perf_counter()
     for i in range(steps):
-        one_step(warmup + i, evs[i])
+        one_step(i)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = {n: [] for n in names}
-    for ev in evs:
-        for j, n in enumerate(names):
-            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)   # us
-    gpu_ms = sum(evs[i][0].elapsed_time(evs[i][5]) for i in range(steps)) / steps
-    del xs, ws
-    torch.cuda.empty_cache()
-    return dict(wall_ms=wall * 1e3 / steps, gpu_ms=gpu_ms,
-                us={n: float(np.mean(v)) for n, v in per.items()},
-                us_median={n: float(np.median(v)) for n, v in per.items()})
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    # the timed region: one replay of a graph of exactly `steps` steps
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one_step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            one_step(i)
+    graph.replay()                       # untimed replay (first-replay setup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    gpu_ms = e0.elapsed_time(e1) / steps
+    del graph
+
+    # each call alone, back to back over the copies, in its own graph
+    calls = 2 * copies
+    us = {"hessian_diag": _graph_time_us(torch, hess, calls),
+          "select_blocks": _graph_time_us(torch, select, calls),
+          "pack_weights": _graph_time_us(torch, pack, calls),
+          "quantize_act": _graph_time_us(torch, quant, calls),
+          "gemm_w4a4_residual": _graph_time_us(torch, gemm, calls)}
+    for n, v in us.items():
+        log(f"[bench] {n}: {v:.3f} us per call")
+    log(f"[bench] step: {gpu_ms * 1e3:.2f} us (graph), {eager_ms * 1e3:.2f} us (eager Python launches)")
+    return dict(gpu_ms=gpu_ms, wall_ms=wall_ms, eager_ms=eager_ms, us=us, copies=copies)
 
 
 def bench_gemm(mq, torch, cfg, inp, k_blocks, calls):
-    """Fused, dense-only and separate-kernel GEMM over rotated packed-weight copies."""
+    """Fused, dense-only and separate-kernel GEMM over rotated packed-weight copies,
+    each in its own HIP graph of `calls` back-to-back calls; every variant's graph
+    output is checked against its eager call."""
     dev = torch.device("cuda:0")
     if inp.X_bits is not None:
         x = torch.from_numpy(inp.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -158,20 +218,21 @@ def bench_gemm(mq, torch, cfg, inp, k_blocks, calls):
     xq, sx, K, bn = g["xq"], g["sx"], cfg.K, cfg.bn
     y = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device=dev)
     wsb = torch.empty((cfg.M, cfg.N), dtype=torch.float32, device=dev)
+    gws = mq.workspace(cfg.M, cfg.N, K, device=dev)
     log(f"[bench] gemm legs: {copies} packed-weight copies ({copies * packed / 2**20:.0f} MiB), "
         f"{calls} calls each")
 
     def fused(i):
         wq, sw, rq, rp, ci = sets[i % copies]
-        mq.gemm_w4a4_residual(xq, sx, wq, sw, rp, ci, rq, K, bn=bn, y=y)
+        mq.gemm_w4a4_residual(xq, sx, wq, sw, rp, ci, rq, K, bn=bn, y=y, workspace=gws)
 
     def dense(i):
         wq, sw, *_ = sets[i % copies]
-        mq.gemm_w4a4_dense(xq, sx, wq, sw, K, y=y)
+        mq.gemm_w4a4_dense(xq, sx, wq, sw, K, y=y, workspace=gws)
 
     def separate(i):
         wq, sw, rq, rp, ci = sets[i % copies]
-        mq.gemm_residual_separate(xq, sx, wq, sw, rp, ci, rq, K, bn=bn, y=y, ws=wsb)
+        mq.gemm_residual_separate(xq, sx, wq, sw, rp, ci, rq, K, bn=bn, y=y, ws=wsb, workspace=gws)
 
     out = {}
     for name, fn in (("dense", dense), ("fused", fused), ("separate", separate)):
@@ -179,32 +240,10 @@ def bench_gemm(mq, torch, cfg, inp, k_blocks, calls):
         fn(calls - 1)
         torch.cuda.synchronize()
         y_eager = y.clone()
-        # capture `calls` back-to-back launches in one HIP graph, so the timing is
-        # the kernels' and not the Python launch path's
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for i in range(3):
-                fn(i)
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(calls):
-                fn(i)
-        reps = []
-        for _ in range(6):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            graph.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
-                raise RuntimeError(f"graph replay of the {name} GEMM differs from the eager call")
-            reps.append(e0.elapsed_time(e1) * 1e3 / calls)
-        reps = reps[1:]
-        out[name] = float(np.median(reps))
-        log(f"[bench] gemm {name}: {out[name]:.3f} us/call (graph replays {[round(r, 3) for r in reps]})")
-        del graph
+        out[name] = _graph_time_us(torch, fn, calls)
+        if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
+            raise RuntimeError(f"graph replay of the {name} GEMM differs from the eager call")
+        log(f"[bench] gemm {name}: {out[name]:.3f} us/call")
     return out
 
 
@@ -323,7 +362,7 @@ def main():
                 "overhead_vs_dense": round(t["fused"] / t["dense"] - 1, 4),
                 "separate_overhead_vs_dense": round(t["separate"] / t["dense"] - 1, 4),
                 "residual_bytes_vs_base": round((fb - db) / (cfg.N * cfg.K // 2 + cfg.N * cfg.K // 64), 4),
-                "timing": "median of 5 HIP-graph replays of %d back-to-back calls over rotated "
+                "timing": "median of 5 replays of a HIP graph of %d back-to-back calls over rotated "
                           "packed-weight copies, HIP events around each replay" % args.gemm_calls}
 
     calib = None if args.no_calib else calibrate(torch)
@@ -343,6 +382,10 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(st["gpu_ms"], 5),
         "wall_ms_per_step": round(st["wall_ms"], 5),
+        "eager_ms_per_step": round(st["eager_ms"], 5),
+        "timing": "one replay of a HIP graph holding exactly `steps` steps (after `warmup` eager "
+                  "steps), HIP events on the launch stream, inputs rotated over %d HBM-resident "
+                  "copies; per-call figures: each call alone in its own graph" % st["copies"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -33,7 +33,7 @@ _p, _i64, _int = C.c_void_p, C.c_int64, C.c_int
 _SIGS = {
     "mq_hessian_diag": [_p, _int, _i64, _i64, _p, _p],
     "mq_quantize_act": [_p, _int, _i64, _i64, _p, _p, _p],
-    "mq_select_blocks": [_p, _p, _i64, _i64, _int, _int, _int, _i64, _p, _p, _p, _p],
+    "mq_select_blocks": [_p, _p, _i64, _i64, _int, _int, _int, _i64, _p, _p, _p, _p, C.c_size_t, _p],
     "mq_pack_weights": [_p, _i64, _i64, _int, _int, _int, _p, _p, _i64, _p, _p, _p, _p],
     "mq_gemm_w4a4_residual": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
                               _p, _int, _p, _p, C.c_size_t, _p],
@@ -50,8 +50,11 @@ _lib.mq_version.argtypes = []
 _lib.mq_version.restype = C.c_int
 _lib.mq_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64]
 _lib.mq_gemm_workspace_bytes.restype = C.c_size_t
+_lib.mq_select_workspace_bytes.argtypes = [_i64, _i64, _int, _int]
+_lib.mq_select_workspace_bytes.restype = C.c_size_t
 
-EXPORTS = tuple(_SIGS) + ("mq_status_string", "mq_version", "mq_gemm_workspace_bytes")
+EXPORTS = tuple(_SIGS) + ("mq_status_string", "mq_version", "mq_gemm_workspace_bytes",
+                          "mq_select_workspace_bytes")
 
 
 class MQError(RuntimeError):
@@ -129,9 +132,17 @@ def quantize_act(x: torch.Tensor, xq: torch.Tensor | None = None, sx: torch.Tens
 
 
 # --------------------------------------------------------------------------- a2
+def select_workspace(N: int, K: int, bn: int = 64, bk: int = BK, device="cuda"):
+    """Scratch for select_blocks (per-block ranks), so the call allocates nothing."""
+    n = int(_lib.mq_select_workspace_bytes(N, K, bn, bk))
+    return torch.empty(max(n, 4), dtype=torch.uint8, device=device)
+
+
 def select_blocks(w: torch.Tensor, h: torch.Tensor, k_blocks: int, bn: int = 64, group: int = GROUP,
-                  bk: int = BK, out=None, stream=None):
-    """Returns (row_ptr int32 [N/bn+1], col_idx int32 [k_blocks], delta fp64 [NB])."""
+                  bk: int = BK, out=None, workspace=None, stream=None):
+    """Returns (row_ptr int32 [N/bn+1], col_idx int32 [k_blocks], delta fp64 [NB]).
+    workspace: optional select_workspace(...) tensor; without it the library takes a
+    stream-ordered allocation for the call."""
     _device_contig(w, "w")
     _device_contig(h, "h")
     N, K = w.shape
@@ -142,8 +153,10 @@ def select_blocks(w: torch.Tensor, h: torch.Tensor, k_blocks: int, bn: int = 64,
         delta = torch.empty(max(nb, 1), dtype=torch.float64, device=w.device)
     else:
         row_ptr, col_idx, delta = out
+    ws = _ptr(workspace) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _call("mq_select_blocks", _ptr(w), _ptr(h), N, K, group, bn, bk, k_blocks, _ptr(row_ptr),
-          _ptr(col_idx), _ptr(delta), _stream(stream))
+          _ptr(col_idx), _ptr(delta), ws, wsb, _stream(stream))
     return row_ptr, col_idx[:k_blocks], delta[:nb]
 
 

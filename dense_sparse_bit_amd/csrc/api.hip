@@ -106,15 +106,23 @@ int mq_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* x
 
 int mq_select_blocks(const float* w, const float* h, int64_t N, int64_t K, int group, int bn, int bk,
                      int64_t k_blocks, int32_t* row_ptr, int32_t* col_idx, double* delta,
-                     void* stream) {
+                     void* workspace, size_t workspace_bytes, void* stream) {
     int rc = check_layer(N, K, group, bn, bk);
     if (rc) return rc;
     const int64_t nb = (N / bn) * (K / bk);
     if (k_blocks < 0 || k_blocks > nb) return MQ_ERR_INVALID_ARG;
     if (!w || !h || !row_ptr || !delta || (k_blocks > 0 && !col_idx) || !aligned16(w) || !aligned16(h))
         return MQ_ERR_INVALID_ARG;
+    if (workspace && (workspace_bytes < static_cast<size_t>(nb) * sizeof(int32_t) ||
+                      (reinterpret_cast<uintptr_t>(workspace) & 3u)))
+        return MQ_ERR_INVALID_ARG;
     return hip_status(mq::launch_select(w, h, N, K, bn, k_blocks, row_ptr, col_idx, delta,
-                                        static_cast<hipStream_t>(stream)));
+                                        static_cast<int32_t*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+size_t mq_select_workspace_bytes(int64_t N, int64_t K, int bn, int bk) {
+    if (check_layer(N, K, mq::kGroup, bn, bk)) return 0;
+    return static_cast<size_t>((N / bn) * (K / bk)) * sizeof(int32_t);
 }
 
 int mq_pack_weights(const float* w, int64_t N, int64_t K, int group, int bn, int bk,

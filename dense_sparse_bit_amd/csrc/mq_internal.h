@@ -35,9 +35,10 @@ size_t gemm_workspace_bytes(int M, int N, int K);
 hipError_t launch_hessian(const void* x, int bf16, int64_t M, int64_t K, float* h, hipStream_t st);
 hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, uint8_t* xq, float* sx,
                             hipStream_t st);
+// rank_ws: nb int32 of scratch, or null for a stream-ordered allocation
 hipError_t launch_select(const float* w, const float* h, int64_t N, int64_t K, int bn,
                          int64_t k_blocks, int32_t* row_ptr, int32_t* col_idx, double* delta,
-                         hipStream_t st);
+                         int32_t* rank_ws, hipStream_t st);
 hipError_t launch_pack(const float* w, int64_t N, int64_t K, int bn, const int32_t* row_ptr,
                        const int32_t* col_idx, int64_t nnz, uint8_t* wq, uint16_t* sw, uint8_t* rq,
                        hipStream_t st);

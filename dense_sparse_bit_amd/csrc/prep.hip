@@ -369,50 +369,43 @@ __global__ __launch_bounds__(256) void k_rank(const double* __restrict__ delta, 
 
 // ---------------------------------------------------------------------------
 // a2 (part 3): CSR of the chosen blocks (rank < k_blocks) in id order, i.e. block
-// row, then column block ascending. One workgroup scans the flags.
+// row, then column block ascending. One workgroup; each thread owns a contiguous
+// run of ids, so one block-wide exclusive scan of the per-thread counts gives
+// every chosen block its CSR position.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_csr(const int32_t* __restrict__ rank, int64_t nb, int64_t nbc,
-                                              int64_t nbr, int64_t k_blocks, int32_t* __restrict__ row_ptr,
+__global__ __launch_bounds__(1024) void k_csr(const int32_t* __restrict__ rank, int nb, int nbc, int nbr,
+                                              int k_blocks, int32_t* __restrict__ row_ptr,
                                               int32_t* __restrict__ col_idx) {
     __shared__ int wsum[16];
-    __shared__ int carry_s;
-    if (threadIdx.x == 0) carry_s = 0;
-    __syncthreads();
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    // flags of the first 32 passes are loaded up front (independent loads)
-    constexpr int kPre = 32;
-    uint32_t pre = 0;
-#pragma unroll
-    for (int i = 0; i < kPre; ++i) {
-        const int64_t id = static_cast<int64_t>(i) * blockDim.x + threadIdx.x;
-        if (id < nb && rank[id] < k_blocks) pre |= 1u << i;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int per = (nb + 1023) / 1024;
+    const int id0 = min(t * per, nb), id1 = min(id0 + per, nb);
+    int cnt = 0;
+    for (int id = id0; id < id1; ++id) cnt += rank[id] < k_blocks;
+    int v = cnt;                                          // inclusive scan in the wavefront
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(v, off);
+        if (lane >= off) v += u;
     }
-    int pass = 0;
-    for (int64_t base = 0; base < nb; base += blockDim.x, ++pass) {
-        const int64_t id = base + threadIdx.x;
-        const int f = id < nb ? (pass < kPre ? static_cast<int>((pre >> pass) & 1u) : (rank[id] < k_blocks)) : 0;
-        // inclusive scan inside the wavefront
-        int v = f;
-        for (int off = 1; off < 64; off <<= 1) {
-            const int u = __shfl_up(v, off);
-            if (lane >= off) v += u;
-        }
-        if (lane == 63) wsum[wv] = v;
-        __syncthreads();
-        int before = carry_s;
-        for (int i = 0; i < wv; ++i) before += wsum[i];
-        const int excl = before + v - f;
-        if (id < nb) {
-            if (id % nbc == 0) row_ptr[id / nbc] = excl;
+    if (lane == 63) wsum[wv] = v;
+    __syncthreads();
+    int pos = v - cnt;
+    for (int i = 0; i < wv; ++i) pos += wsum[i];
+    int row = id0 / nbc, col = id0 - row * nbc;
+    for (int id = id0; id < id1; ++id) {
+        if (col == 0) row_ptr[row] = pos;
+        if (rank[id] < k_blocks) {
             // ranks form a permutation, so exactly k_blocks flags are set; the
             // bound only matters for non-finite scores (unsupported inputs)
-            if (f && excl < k_blocks) col_idx[excl] = static_cast<int32_t>(id % nbc);
+            if (pos < k_blocks) col_idx[pos] = col;
+            ++pos;
         }
-        __syncthreads();
-        if (threadIdx.x == blockDim.x - 1) carry_s = excl + f;
-        __syncthreads();
+        if (++col == nbc) {
+            col = 0;
+            ++row;
+        }
     }
-    if (threadIdx.x == 0) row_ptr[nbr] = carry_s;
+    if (t == 1023) row_ptr[nbr] = pos;                    // the last thread ends at the total
 }
 
 // ---------------------------------------------------------------------------
@@ -552,11 +545,14 @@ hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, uint8
 
 hipError_t launch_select(const float* w, const float* h, int64_t N, int64_t K, int bn,
                          int64_t k_blocks, int32_t* row_ptr, int32_t* col_idx, double* delta,
-                         hipStream_t st) {
+                         int32_t* rank_ws, hipStream_t st) {
     const int64_t nbr = N / bn, nbc = K / kBk, nb = nbr * nbc;
-    int32_t* rank = nullptr;
-    hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&rank), static_cast<size_t>(nb) * sizeof(int32_t), st);
-    if (err != hipSuccess) return err;
+    int32_t* rank = rank_ws;
+    hipError_t err = hipSuccess;
+    if (!rank) {
+        err = hipMallocAsync(reinterpret_cast<void**>(&rank), static_cast<size_t>(nb) * sizeof(int32_t), st);
+        if (err != hipSuccess) return err;
+    }
     // about four workgroups per CU: each walks nbr / P block rows of one group
     const int64_t G = K / kGroup;
     const int64_t P = std::max<int64_t>(1, std::min<int64_t>(nbr, (1024 + G - 1) / G));
@@ -570,9 +566,11 @@ hipError_t launch_select(const float* w, const float* h, int64_t N, int64_t K, i
         err = hipGetLastError();
     }
     if (err == hipSuccess) {
-        k_csr<<<dim3(1), dim3(1024), 0, st>>>(rank, nb, nbc, nbr, k_blocks, row_ptr, col_idx);
+        k_csr<<<dim3(1), dim3(1024), 0, st>>>(rank, static_cast<int>(nb), static_cast<int>(nbc),
+                                              static_cast<int>(nbr), static_cast<int>(k_blocks), row_ptr, col_idx);
         err = hipGetLastError();
     }
+    if (rank_ws) return err;
     const hipError_t ferr = hipFreeAsync(rank, st);
     return err != hipSuccess ? err : ferr;
 }

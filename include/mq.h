@@ -100,11 +100,17 @@ int mq_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* x
  *   row_ptr: int32 [N/bn + 1], col_idx: int32 [k_blocks] (column-block index,
  *   ascending within a row), delta: fp64 [NB] with NB = (N/bn)*(K/bk).
  * w: fp32 [N][K], h: fp32 [K]. 0 <= k_blocks <= NB.
- * Uses stream-ordered temporary device memory (hipMallocAsync) of NB bytes.
+ * workspace: device scratch of at least mq_select_workspace_bytes(N, K, bn, bk) bytes
+ * (4 * NB, 4-byte aligned; the per-block ranks), or NULL: the call then takes a
+ * stream-ordered allocation (hipMallocAsync) and releases it on the same stream.
+ * Calls sharing one workspace must be ordered on one stream.
  */
 int mq_select_blocks(const float* w, const float* h, int64_t N, int64_t K, int group, int bn,
                      int bk, int64_t k_blocks, int32_t* row_ptr, int32_t* col_idx,
-                     double* delta, void* stream);
+                     double* delta, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mq_select_blocks needs for this shape (0 for an unsupported shape). */
+size_t mq_select_workspace_bytes(int64_t N, int64_t K, int bn, int bk);
 
 /*
  * Packs the dense 4-bit base for every group and the 4-bit residual payload for

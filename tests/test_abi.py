@@ -34,7 +34,7 @@ def mq():
 def test_header_declares_the_boundary():
     names = _declared()
     for fn in ["mq_quantize_act", "mq_pack_weights", "mq_select_blocks", "mq_gemm_w4a4_residual",
-               "mq_gemm_workspace_bytes",
+               "mq_gemm_workspace_bytes", "mq_select_workspace_bytes",
                "mq_hessian_diag", "mq_gemm_w4a4_dense", "mq_gemm_residual_separate",
                "mq_status_string", "mq_version"]:
         assert fn in names
@@ -97,10 +97,16 @@ def test_preparation_calls_reject_bad_arguments(lib_nogpu):
     assert lib.mq_hessian_diag(FAKE, 1, 0, 512, FAKE, None) == -1
     assert lib.mq_hessian_diag(None, 1, 4, 512, FAKE, None) == -1
     nb = (512 // 64) * (512 // 64)
-    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, nb + 1, FAKE, FAKE, FAKE, None) == -1
-    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, -1, FAKE, FAKE, FAKE, None) == -1
-    assert lib.mq_select_blocks(FAKE, FAKE, 512, 500, 128, 64, 64, 3, FAKE, FAKE, FAKE, None) == -2
-    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, 3, FAKE, FAKE, None, None) == -1
+    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, nb + 1, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, -1, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert lib.mq_select_blocks(FAKE, FAKE, 512, 500, 128, 64, 64, 3, FAKE, FAKE, FAKE, None, 0, None) == -2
+    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, 3, FAKE, FAKE, None, None, 0, None) == -1
+    # a workspace smaller than the per-block ranks, or misaligned, is rejected before any launch
+    assert lib.mq_select_workspace_bytes(512, 512, 64, 64) == 4 * nb
+    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, 3, FAKE, FAKE, FAKE, FAKE,
+                                4 * nb - 1, None) == -1
+    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, 3, FAKE, FAKE, FAKE, FAKE + 2,
+                                4 * nb, None) == -1
     assert lib.mq_pack_weights(FAKE, 512, 512, 128, 64, 64, None, FAKE, 3, FAKE, FAKE, FAKE, None) == -1
     assert lib.mq_pack_weights(FAKE + 4, 512, 512, 128, 64, 64, FAKE, FAKE, 3, FAKE, FAKE, FAKE, None) == -1
     assert lib.mq_gemm_w4a4_dense(FAKE, FAKE, FAKE, FAKE, 4, 512, 320, 128, FAKE, 0, None, None, 0,
