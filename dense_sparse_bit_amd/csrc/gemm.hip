@@ -64,24 +64,26 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int OUTMODE, int m,
 constexpr int kMaxDecodeWaves = 8;
 constexpr int kMaxGroups = 512;    // K <= 65536
 
-template <int MT>
+// One pipeline step: QS consecutive groups (QS = 4 for one row tile of tokens,
+// 2 for two, which keeps two steps' registers within three waves per SIMD).
+template <int MT, int QS>
 struct DecStep {
-    uint4 w[4];        // base nibbles of the quad's four groups
-    uint4 x[MT][4];    // activation nibbles
-    uint4 r[4];        // residual nibbles (zero where no chosen block)
-    uint2 s;           // the row's four fp16 group scales
-    int rg;            // bit u: group 4q+u holds a chosen block in this block row
+    uint4 w[QS];         // base nibbles of the step's groups
+    uint4 x[MT][QS];     // activation nibbles
+    uint4 r[QS];         // residual nibbles (zero where no chosen block)
+    uint32_t s[QS / 2];  // the row's fp16 group scales, two per word
+    int rg;              // bit u: group g0+u holds a chosen block in this block row
 };
 
-// base tiles, activations and scales of quad q
-template <int MT>
-__device__ __forceinline__ void dec_fetch_main(DecStep<MT>& st, const GemmArgs& a, int nt, int G, int G4, int q,
+// base tiles, activations and scales of the step starting at group g0
+template <int MT, int QS>
+__device__ __forceinline__ void dec_fetch_main(DecStep<MT, QS>& st, const GemmArgs& a, int nt, int G, int G4, int g0,
                                                int lane) {
     const int li = lane & 15, kg = lane >> 4;
     const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int g = 4 * q + u;
+    for (int u = 0; u < QS; ++u) {
+        const int g = g0 + u;
         const bool ok = g < G;
         st.w[u] = ok ? ldg16(a.wq + wq_tile(nt, G, g) + lane * 16) : z;
 #pragma unroll
@@ -90,22 +92,32 @@ __device__ __forceinline__ void dec_fetch_main(DecStep<MT>& st, const GemmArgs& 
             st.x[t][u] = ok && m < a.M ? ldg16(a.xq + xq_row(g, a.M, m) + kg * 16) : z;
         }
     }
-    st.s = *reinterpret_cast<const uint2*>(a.sw + ((static_cast<int64_t>(nt) * G4 + q) * 16 + li) * 4);
+    const uint16_t* sp = a.sw + ((static_cast<int64_t>(nt) * G4 + (g0 >> 2)) * 16 + li) * 4 + (g0 & 3);
+    if (QS == 4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(sp);
+        st.s[0] = v.x;
+        st.s[QS / 2 - 1] = v.y;
+    } else {
+        st.s[0] = *reinterpret_cast<const uint32_t*>(sp);
+    }
 }
 
-// residual rows of quad q: the zipper table gives each column block's CSR
+// residual rows of the step: the zipper table gives each column block's CSR
 // position (or -1); lanes 0-31 take the group's first block, 32-63 the second
-template <int MT, bool RES>
-__device__ __forceinline__ void dec_fetch_res(DecStep<MT>& st, const GemmArgs& a, const int* tab, int rrow, int G,
-                                              int q, int lane) {
+template <int MT, int QS, bool RES>
+__device__ __forceinline__ void dec_fetch_res(DecStep<MT, QS>& st, const GemmArgs& a, const int* tab, int rrow,
+                                              int G, int g0, int lane) {
     const int kg = lane >> 4;
     st.rg = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int g = 4 * q + u;
+    for (int u = 0; u < QS; ++u) {
+        const int g = g0 + u;
         st.r[u] = make_uint4(0, 0, 0, 0);
         if (RES && g < G) {
-            const int j0 = tab[2 * g], j1 = tab[2 * g + 1];
+            // the table entry is the same for the whole wave: make that visible to
+            // the compiler, so the residual branch in dec_compute is a scalar one
+            const int j0 = __builtin_amdgcn_readfirstlane(tab[2 * g]);
+            const int j1 = __builtin_amdgcn_readfirstlane(tab[2 * g + 1]);
             if (j0 >= 0 || j1 >= 0) st.rg |= 1 << u;
             const int j = kg < 2 ? j0 : j1;
             if (j >= 0) st.r[u] = ldg16(a.rq + (static_cast<int64_t>(j) * a.bn + rrow) * 32 + (kg & 1) * 16);
@@ -113,27 +125,24 @@ __device__ __forceinline__ void dec_fetch_res(DecStep<MT>& st, const GemmArgs& a
     }
 }
 
-template <int MT, bool RES, bool DUMP>
-__device__ __forceinline__ void dec_compute(const DecStep<MT>& st, const GemmArgs& a, int n, int G, int q,
+template <int MT, int QS, bool RES, bool DUMP>
+__device__ __forceinline__ void dec_compute(const DecStep<MT, QS>& st, const GemmArgs& a, int n, int G, int g0,
                                             int lane, float (&acc)[MT][4]) {
     const int kg = lane >> 4;
-    const float sc[4] = {f16_bits_to_f32(static_cast<uint16_t>(st.s.x)),
-                         f16_bits_to_f32(static_cast<uint16_t>(st.s.x >> 16)),
-                         f16_bits_to_f32(static_cast<uint16_t>(st.s.y)),
-                         f16_bits_to_f32(static_cast<uint16_t>(st.s.y >> 16))};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int g = 4 * q + u;
+    for (int u = 0; u < QS; ++u) {
+        const int g = g0 + u;
         if (g >= G) break;
+        const float sc = f16_bits_to_f32(static_cast<uint16_t>(st.s[u >> 1] >> (16 * (u & 1))));
         const bool res = RES && ((st.rg >> u) & 1);
         v4i b0, b1;
         float scale;
         if (res) {
             unpack_comb(st.w[u], st.r[u], b0, b1);
-            scale = (sc[u] / 14.0f) * 0.0625f;
+            scale = (sc / 14.0f) * 0.0625f;
         } else {
             unpack16(st.w[u], b0, b1);
-            scale = sc[u] * 0.00390625f;
+            scale = sc * 0.00390625f;
         }
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
@@ -158,29 +167,31 @@ __device__ __forceinline__ void dec_compute(const DecStep<MT>& st, const GemmArg
 
 template <int MT, bool RES, bool DUMP, int OUTMODE>
 __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a) {
+    constexpr int QS = MT == 1 ? 4 : 2;
     __shared__ float red[kMaxDecodeWaves * MT * 256];
     __shared__ int tab[RES ? 8 * (kMaxGroups / 4) : 1];   // column block -> CSR position
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     const int G = a.K / kGroup, G4 = (G + 3) / 4;
     const int nt = blockIdx.x, n0 = nt * 16, n = n0 + (lane & 15);
     const int br = n0 / a.bn, rrow = n - br * a.bn;
-    const int q0 = wave * G4 / nw, q1 = (wave + 1) * G4 / nw;
+    const int q0 = wave * G4 / nw, q1 = (wave + 1) * G4 / nw;       // this wave's quads
+    const int gb = 4 * q0, ge = min(4 * q1, G);                      // and groups
     float acc[MT][4];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
 
-    // two quads in flight: quad q+1 is fetched while q is multiplied (ping-pong
-    // buffers, so no register copy waits on the prefetch)
-    DecStep<MT> s0, s1;
-    if (q0 < q1) dec_fetch_main<MT>(s0, a, nt, G, G4, q0, lane);
+    // two steps in flight: step i+1 is fetched while step i is multiplied
+    // (ping-pong buffers, so no register copy waits on the prefetch)
+    DecStep<MT, QS> s0, s1;
+    if (gb < ge) dec_fetch_main<MT, QS>(s0, a, nt, G, G4, gb, lane);
     if (RES) {
-        // The zipper table of this wave's column blocks [8 q0, 8 q1), built by the
+        // The zipper table of this wave's column blocks [2 gb, 2 ge), built by the
         // wave alone while its first loads are in flight: no workgroup barrier.
         // A wavefront's LDS operations complete in issue order, so the -1 fill,
         // the CSR positions and the later reads need no wait between lanes.
-        const int kb0 = 8 * q0, kb1 = min(8 * q1, 2 * G);
+        const int kb0 = 2 * gb, kb1 = 2 * ge;
         for (int i = kb0 + lane; i < kb1; i += 64) tab[i] = -1;
         __builtin_amdgcn_wave_barrier();
         const int lo = clampi(a.row_ptr[br], 0, a.nnz);
@@ -190,20 +201,20 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
             if (kb >= kb0 && kb < kb1) tab[kb] = i;
         }
         __builtin_amdgcn_wave_barrier();
-        if (q0 < q1) dec_fetch_res<MT, RES>(s0, a, tab, rrow, G, q0, lane);
+        if (gb < ge) dec_fetch_res<MT, QS, RES>(s0, a, tab, rrow, G, gb, lane);
     }
-    for (int q = q0; q < q1; q += 2) {
-        if (q + 1 < q1) {
-            dec_fetch_main<MT>(s1, a, nt, G, G4, q + 1, lane);
-            if (RES) dec_fetch_res<MT, RES>(s1, a, tab, rrow, G, q + 1, lane);
+    for (int g = gb; g < ge; g += 2 * QS) {
+        if (g + QS < ge) {
+            dec_fetch_main<MT, QS>(s1, a, nt, G, G4, g + QS, lane);
+            if (RES) dec_fetch_res<MT, QS, RES>(s1, a, tab, rrow, G, g + QS, lane);
         }
-        dec_compute<MT, RES, DUMP>(s0, a, n, G, q, lane, acc);
-        if (q + 1 >= q1) break;
-        if (q + 2 < q1) {
-            dec_fetch_main<MT>(s0, a, nt, G, G4, q + 2, lane);
-            if (RES) dec_fetch_res<MT, RES>(s0, a, tab, rrow, G, q + 2, lane);
+        dec_compute<MT, QS, RES, DUMP>(s0, a, n, G, g, lane, acc);
+        if (g + QS >= ge) break;
+        if (g + 2 * QS < ge) {
+            dec_fetch_main<MT, QS>(s0, a, nt, G, G4, g + 2 * QS, lane);
+            if (RES) dec_fetch_res<MT, QS, RES>(s0, a, tab, rrow, G, g + 2 * QS, lane);
         }
-        dec_compute<MT, RES, DUMP>(s1, a, n, G, q + 1, lane, acc);
+        dec_compute<MT, QS, RES, DUMP>(s1, a, n, G, g + QS, lane, acc);
     }
 
 #pragma unroll
