@@ -75,38 +75,41 @@ struct DecStep {
     int rg;              // bit u: group g0+u holds a chosen block in this block row
 };
 
-// base tiles, activations and scales of the step starting at group g0
+// Per-wave buffer resources and lane offsets of the decode operands.
+struct DecSrc {
+    __amdgpu_buffer_rsrc_t w, x, s, r;   // this subtile's tiles, all activations, this subtile's
+                                         // scales, this block row's residual payload
+    uint32_t xrow[2];                    // lane's activation row offset per row tile
+    uint32_t xstride;                    // bytes per group of activations (M * 64)
+    int lo;                              // first CSR position of the block row
+};
+
+// base tiles, activations and scales of the step starting at group g0 (groups
+// past the last read zero through the range check)
 template <int MT, int QS>
-__device__ __forceinline__ void dec_fetch_main(DecStep<MT, QS>& st, const GemmArgs& a, int nt, int G, int G4, int g0,
-                                               int lane) {
-    const int li = lane & 15, kg = lane >> 4;
-    const uint4 z = make_uint4(0, 0, 0, 0);
+__device__ __forceinline__ void dec_fetch_main(DecStep<MT, QS>& st, const DecSrc& src, int g0, int lane) {
 #pragma unroll
     for (int u = 0; u < QS; ++u) {
-        const int g = g0 + u;
-        const bool ok = g < G;
-        st.w[u] = ok ? ldg16(a.wq + wq_tile(nt, G, g) + lane * 16) : z;
+        const uint32_t g = g0 + u;
+        st.w[u] = buf_load16(src.w, g * 1024u + lane * 16u);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const int m = t * 16 + li;
-            st.x[t][u] = ok && m < a.M ? ldg16(a.xq + xq_row(g, a.M, m) + kg * 16) : z;
-        }
+        for (int t = 0; t < MT; ++t) st.x[t][u] = buf_load16(src.x, g * src.xstride + src.xrow[t]);
     }
-    const uint16_t* sp = a.sw + ((static_cast<int64_t>(nt) * G4 + (g0 >> 2)) * 16 + li) * 4 + (g0 & 3);
+    const uint32_t so = (g0 >> 2) * 128u + (lane & 15) * 8u + (g0 & 3) * 2u;
     if (QS == 4) {
-        const uint2 v = *reinterpret_cast<const uint2*>(sp);
+        const uint2 v = buf_load8(src.s, so);
         st.s[0] = v.x;
         st.s[QS / 2 - 1] = v.y;
     } else {
-        st.s[0] = *reinterpret_cast<const uint32_t*>(sp);
+        st.s[0] = buf_load4(src.s, so);
     }
 }
 
 // residual rows of the step: the zipper table gives each column block's CSR
 // position (or -1); lanes 0-31 take the group's first block, 32-63 the second
 template <int MT, int QS, bool RES>
-__device__ __forceinline__ void dec_fetch_res(DecStep<MT, QS>& st, const GemmArgs& a, const int* tab, int rrow,
-                                              int G, int g0, int lane) {
+__device__ __forceinline__ void dec_fetch_res(DecStep<MT, QS>& st, const GemmArgs& a, const DecSrc& src,
+                                              const int* tab, int rrow, int G, int g0, int lane) {
     const int kg = lane >> 4;
     st.rg = 0;
 #pragma unroll
@@ -118,9 +121,13 @@ __device__ __forceinline__ void dec_fetch_res(DecStep<MT, QS>& st, const GemmArg
             // the compiler, so the residual branch in dec_compute is a scalar one
             const int j0 = __builtin_amdgcn_readfirstlane(tab[2 * g]);
             const int j1 = __builtin_amdgcn_readfirstlane(tab[2 * g + 1]);
-            if (j0 >= 0 || j1 >= 0) st.rg |= 1 << u;
-            const int j = kg < 2 ? j0 : j1;
-            if (j >= 0) st.r[u] = ldg16(a.rq + (static_cast<int64_t>(j) * a.bn + rrow) * 32 + (kg & 1) * 16);
+            if (j0 >= 0 || j1 >= 0) {
+                st.rg |= 1 << u;
+                const int j = kg < 2 ? j0 : j1;
+                // no block: an offset past the range reads zero
+                const uint32_t off = j >= 0 ? ((j - src.lo) * a.bn + rrow) * 32u + (kg & 1) * 16u : 0xFFFFFFF0u;
+                st.r[u] = buf_load16(src.r, off);
+            }
         }
     }
 }
@@ -182,10 +189,24 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
 
+    const int lo = RES ? clampi(a.row_ptr[br], 0, a.nnz) : 0;
+    const int hi = RES ? clampi(a.row_ptr[br + 1], lo, a.nnz) : 0;
+    DecSrc src;
+    src.w = buf_rsrc(a.wq + wq_tile(nt, G, 0), static_cast<uint32_t>(G) * 1024u);
+    src.x = buf_rsrc(a.xq, static_cast<uint32_t>(a.M) * static_cast<uint32_t>(a.K / 2));
+    src.s = buf_rsrc(a.sw + static_cast<int64_t>(nt) * G4 * 64, static_cast<uint32_t>(G4) * 128u);
+    src.r = buf_rsrc(RES && hi > lo ? a.rq + static_cast<int64_t>(lo) * a.bn * 32 : a.wq,
+                     RES ? static_cast<uint32_t>(hi - lo) * static_cast<uint32_t>(a.bn) * 32u : 0u);
+    src.xstride = static_cast<uint32_t>(a.M) * 64u;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        src.xrow[t] = static_cast<uint32_t>(min(t * 16 + (lane & 15), a.M - 1)) * 64u + (lane >> 4) * 16u;
+    src.lo = lo;
+
     // two steps in flight: step i+1 is fetched while step i is multiplied
     // (ping-pong buffers, so no register copy waits on the prefetch)
     DecStep<MT, QS> s0, s1;
-    if (gb < ge) dec_fetch_main<MT, QS>(s0, a, nt, G, G4, gb, lane);
+    if (gb < ge) dec_fetch_main<MT, QS>(s0, src, gb, lane);
     if (RES) {
         // The zipper table of this wave's column blocks [2 gb, 2 ge), built by the
         // wave alone while its first loads are in flight: no workgroup barrier.
@@ -194,25 +215,23 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
         const int kb0 = 2 * gb, kb1 = 2 * ge;
         for (int i = kb0 + lane; i < kb1; i += 64) tab[i] = -1;
         __builtin_amdgcn_wave_barrier();
-        const int lo = clampi(a.row_ptr[br], 0, a.nnz);
-        const int hi = clampi(a.row_ptr[br + 1], lo, a.nnz);
         for (int i = lo + lane; i < hi; i += 64) {
             const int kb = a.col_idx[i];
             if (kb >= kb0 && kb < kb1) tab[kb] = i;
         }
         __builtin_amdgcn_wave_barrier();
-        if (gb < ge) dec_fetch_res<MT, QS, RES>(s0, a, tab, rrow, G, gb, lane);
+        if (gb < ge) dec_fetch_res<MT, QS, RES>(s0, a, src, tab, rrow, G, gb, lane);
     }
     for (int g = gb; g < ge; g += 2 * QS) {
         if (g + QS < ge) {
-            dec_fetch_main<MT, QS>(s1, a, nt, G, G4, g + QS, lane);
-            if (RES) dec_fetch_res<MT, QS, RES>(s1, a, tab, rrow, G, g + QS, lane);
+            dec_fetch_main<MT, QS>(s1, src, g + QS, lane);
+            if (RES) dec_fetch_res<MT, QS, RES>(s1, a, src, tab, rrow, G, g + QS, lane);
         }
         dec_compute<MT, QS, RES, DUMP>(s0, a, n, G, g, lane, acc);
         if (g + QS >= ge) break;
         if (g + 2 * QS < ge) {
-            dec_fetch_main<MT, QS>(s0, a, nt, G, G4, g + 2 * QS, lane);
-            if (RES) dec_fetch_res<MT, QS, RES>(s0, a, tab, rrow, G, g + 2 * QS, lane);
+            dec_fetch_main<MT, QS>(s0, src, g + 2 * QS, lane);
+            if (RES) dec_fetch_res<MT, QS, RES>(s0, a, src, tab, rrow, G, g + 2 * QS, lane);
         }
         dec_compute<MT, QS, RES, DUMP>(s1, a, n, G, g + QS, lane, acc);
     }

@@ -169,6 +169,32 @@ __device__ __forceinline__ uint4 ldg16(const uint8_t* p) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// ---- raw buffer loads ------------------------------------------------------
+// A buffer resource (base in scalar registers, byte range `bytes`) turns every
+// 16-byte load into one instruction with a 32-bit per-lane offset: no 64-bit
+// address arithmetic per load. The hardware range check covers the per-lane
+// offset: a load at or past `bytes` returns zero, which also replaces the
+// in-range test for a step that runs past the last group.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kBufferFlags = 0x00020000;   // dword 3 of a raw (untyped) gfx9 buffer resource
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), kBufferFlags);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+}
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+    return make_uint2(v.x, v.y);
+}
+
 // ---- device layouts of the packed operands --------------------------------
 // Every 64-lane load of a GEMM operand is 1 KB of contiguous memory in MFMA lane
 // order, so each request the vector memory pipeline carries is fully used:
