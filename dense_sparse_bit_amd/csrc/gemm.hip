@@ -174,7 +174,7 @@ __device__ __forceinline__ void dec_compute(const DecStep<MT, QS>& st, const Gem
 
 template <int MT, bool RES, bool DUMP, int OUTMODE>
 __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a) {
-    constexpr int QS = MT == 1 ? 4 : 2;
+    constexpr int QS = 2;
     __shared__ float red[kMaxDecodeWaves * MT * 256];
     __shared__ int tab[RES ? 8 * (kMaxGroups / 4) : 1];   // column block -> CSR position
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
