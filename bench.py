@@ -306,6 +306,114 @@ def cpu_baseline(cfg, inp, k_blocks, seconds, step_total_bytes):
             "s_per_step": per}
 
 
+# --------------------------------------------------------------------------- profiles
+CALIB_COPY_BYTES = 256 << 20     # the copy of known size the HBM counters are scaled by
+
+
+def pmc_pass(mq, torch, cfg, inp, k_blocks):
+    """What `rocprofv3 --pmc` runs: a few whole steps, then CALIB_COPY_BYTES copied
+    device to device five times (a plain copy of known size, to scale the counters)."""
+    bench_step(mq, torch, cfg, inp, k_blocks, steps=3, warmup=1)
+    src = torch.ones(CALIB_COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)                       # the runtime's blit copy
+    fsrc, fdst = src.view(torch.float32), dst.view(torch.float32)
+    for _ in range(5):
+        torch.mul(fsrc, 1.0, out=fdst)       # an elementwise kernel with 16-byte lane accesses
+    torch.cuda.synchronize()
+
+
+def _db(path):
+    import glob
+    import sqlite3
+    dbs = [path] if path.endswith(".db") else sorted(glob.glob(os.path.join(path, "**", "*.db"), recursive=True))
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 results database under {path}")
+    return sqlite3.connect(dbs[0])
+
+
+def profile_summary(db_path, title, command):
+    """Kernel-trace statistics of a rocprofv3 results database, as text."""
+    con = _db(db_path)
+    rows = list(con.execute("select name, total_calls, total_duration, average, percentage from top_kernels"))
+    out = [f"# {title}", "", f"command: {command}", "",
+           "rocprofv3 --kernel-trace --stats, kernel durations (us):", "",
+           f"{'calls':>6} {'avg_us':>10} {'total_us':>11} {'pct':>6}  kernel"]
+    for name, calls, tot, avg, pct in rows:
+        out.append(f"{calls:>6} {avg:>10.3f} {tot:>11.1f} {pct:>6.2f}  {name[:110]}")
+    return "\n".join(out)
+
+
+def _counter_means(db_path, counter):
+    """Mean of one counter per kernel name, and per-dispatch values of the two copy
+    kernels (runtime blit, elementwise multiply by one)."""
+    con = _db(db_path)
+    per, blit, elem = {}, [], []
+    for k, c, v, grid in con.execute(
+            "select kernel_name, counter_name, value, grid_size from counters_collection"):
+        if c != counter:
+            continue
+        per.setdefault(k, []).append(v)
+        if "copyBuffer" in k:
+            blit.append((grid, v))
+        if "elementwise" in k and "Mul" in k:
+            elem.append((grid, v))
+    return {k: sum(v) / len(v) for k, v in per.items()}, blit, elem
+
+
+def pmc_summary(fetch_db, write_db, title, commands):
+    """HBM traffic per dispatch from FETCH_SIZE and WRITE_SIZE passes, each scaled by
+    what the same counter reads for the largest copy (CALIB_COPY_BYTES each way)."""
+    fetch, fblit, felem = _counter_means(fetch_db, "FETCH_SIZE")
+    write, wblit, welem = _counter_means(write_db, "WRITE_SIZE")
+    kib = CALIB_COPY_BYTES / 1024
+
+    def largest(pairs):
+        big = max(g for g, _ in pairs)
+        return float(np.mean([v for g, v in pairs if g == big]))
+    bf, bw = largest(fblit), largest(wblit)
+    cf, cw = largest(felem), largest(welem)
+    ff, fw = kib / cf, kib / cw
+    import hashlib
+    digest = hashlib.sha256(open(os.path.join(ROOT, "dense_sparse_bit_amd", "csrc", "prep.hip"), "rb")
+                            .read()).hexdigest()[:16]
+    out = [f"# {title}", "", "commands:"] + [f"  {c}" for c in commands] + [
+        "", f"kernel source (dense_sparse_bit_amd/csrc/prep.hip) source sha256: {digest}"] + [
+        "", f"calibration: {CALIB_COPY_BYTES >> 20} MiB read and written by an elementwise kernel "
+        f"(y = x * 1, 16-byte lane accesses like this library's): FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE "
+        f"{cw:.0f} KiB per dispatch -> scale factors {ff:.4f} (fetch), {fw:.4f} (write), used below",
+        f"(the runtime blit copy of the same size reads FETCH_SIZE {bf:.0f} KiB, WRITE_SIZE {bw:.0f} KiB: "
+        f"factors {kib / bf:.4f}, {kib / bw:.4f}; its request sizes differ)", "",
+        f"{'fetch_KiB':>12} {'write_KiB':>12} {'scaled_MB':>10}  kernel"]
+    for k in sorted(set(fetch) | set(write), key=lambda n: -fetch.get(n, 0)):
+        if "mq::" not in k:
+            continue
+        f, w = fetch.get(k, 0.0), write.get(k, 0.0)
+        out.append(f"{f:>12.1f} {w:>12.1f} {(f * ff + w * fw) * 1024 / 1e6:>10.3f}  {k[:100]}")
+    return "\n".join(out)
+
+
+def traffic_from_profile(kernels, source):
+    """HBM bytes per call of the given kernels from the committed counter summary,
+    or None when the summary is missing or was taken from different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "select_blocks_llama3_8b_qo_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    digest = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()[:16]
+    if f"source sha256: {digest}" not in text:
+        return None
+    total = 0.0
+    for k in kernels:
+        line = [l for l in text.splitlines() if l.rstrip().endswith(k) or f" {k}(" in l]
+        if not line:
+            return None
+        total += float(line[0].split()[2]) * 1e6
+    return total
+
+
 # --------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -319,7 +427,20 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-calib", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="run a few steps and a copy of known size (for rocprofv3 --pmc), print nothing")
+    ap.add_argument("--profile-summary", metavar="DB", help="print a rocprofv3 kernel-trace summary")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="print HBM traffic per kernel from FETCH_SIZE and WRITE_SIZE passes")
+    ap.add_argument("--title", default="")
+    ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
+    if args.profile_summary:
+        print(profile_summary(args.profile_summary, args.title, " ; ".join(args.command)))
+        return
+    if args.pmc_summary:
+        print(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.title, args.command))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU leg in this build)", file=sys.stderr)
@@ -334,6 +455,9 @@ def main():
     pct = cfg.default_budget if args.budget is None else args.budget
     k_blocks = cfg.k_blocks(pct)
     inp = synth.make_inputs(cfg)
+    if args.pmc_pass:
+        pmc_pass(mq, torch, cfg, inp, k_blocks)
+        return
     x_bytes = 2 if inp.X_bits is not None else 4
     sb = step_bytes(cfg, k_blocks, x_bytes)
     total_bytes = sum(sb.values())
@@ -373,6 +497,11 @@ def main():
         cpu = cpu_baseline(cfg, inp, k_blocks, args.cpu_seconds, total_bytes)
 
     dom_b = sb[dom]
+    traffic = None
+    if dom == "select_blocks":
+        t = traffic_from_profile(["mq::k_delta", "mq::k_rank", "mq::k_csr"],
+                                 os.path.join("dense_sparse_bit_amd", "csrc", "prep.hip"))
+        traffic = None if t is None else int(t)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -401,8 +530,12 @@ def main():
                            "gemm_w4a4_residual"},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_b / st["us"][dom] / 1e3, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_b / st["us"][dom] / 1e3 / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": dom_b, "us_per_launch": round(st["us"][dom], 3)},
+                     "frac": round(dom_b / st["us"][dom] / 1e3 / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "bytes_per_launch": dom_b, "us_per_launch": round(st["us"][dom], 3),
+                     "traffic_source": "profiles/select_blocks_llama3_8b_qo_hbm_traffic.txt (rocprofv3 "
+                                       "FETCH_SIZE and WRITE_SIZE passes, scaled by a copy of known size; "
+                                       "null when the kernel source changed since)"},
         "cpu_baseline": None if cpu is None else {k: (round(v, 4) if isinstance(v, float) else v)
                                                   for k, v in cpu.items() if k != "s_per_step"},
         "step_kernels": kernels,
