@@ -251,94 +251,119 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
 }
 
 // ===========================================================================
-// Tiled kernel, M > 32 (prefill). 128 x 128 output tile per workgroup, four
-// waves of 64 x 64, one K group per step. The activation and base-weight tiles
-// of the next group, and the residual rows it needs, are fetched into registers
-// while the current group's tiles are consumed from LDS (double buffer, one
-// barrier per group).
+// Prefill kernel, M > 32: 128 x 128 output tile per workgroup, four waves of
+// 64 x 64, one K group per step, two LDS stages.
+//   * The weight tile is staged in LDS as int8 MFMA operands: the staging
+//     threads widen each 16-byte nibble piece once per workgroup, to 16 q for
+//     plain groups or to 14 q + r where the row's block is a chosen residual
+//     block (its residual row is fetched with the base piece). The zipper walk
+//     thus happens at staging; the waves' MFMA loop is the same with or without
+//     residual blocks.
+//   * Each column's dequantization factor for the group (s/256, or s_r/16 in a
+//     residual group) is staged beside the tile.
+//   * The activation tile stays as nibbles in LDS (half the bytes the waves read)
+//     and is widened in registers.
+//   * Global loads of group g+1 are issued before group g's MFMAs and written to
+//     the other LDS stage after them: one barrier per group.
 // ===========================================================================
-constexpr int kBM = 128, kBN = 128;
-constexpr int kRowB = 80;          // LDS bytes per tile row: 64 data + 16 pad (conflict-free b128 reads)
-constexpr int kMaxKb = 1024;       // column blocks per row the LDS zipper table holds (K <= 65536)
+constexpr int kPM = 128, kPN = 128;
+constexpr int kApitch = 80;        // LDS bytes per activation row: 64 nibble bytes + 16 pad
+constexpr int kBpitch = 144;       // LDS bytes per weight row: 128 int8 operand bytes + 16 pad
+
+struct PrefillSmem {
+    static constexpr size_t a_bytes = 2 * kPM * kApitch;
+    static constexpr size_t b_bytes = 2 * kPN * kBpitch;
+    static constexpr size_t f_bytes = 2 * kPN * sizeof(float);
+    static constexpr size_t r_bytes = 2 * kPN;
+    static size_t total(bool res, int G) { return a_bytes + b_bytes + f_bytes + r_bytes + (res ? 2 * 2 * G * sizeof(int) : 0); }
+};
 
 template <bool RES, bool DUMP, int OUTMODE>
-__global__ __launch_bounds__(256, (RES || DUMP) ? 1 : 2) void k_gemm_tiled(GemmArgs a) {
-    __shared__ __align__(16) uint8_t As[2][kBM * kRowB];
-    __shared__ __align__(16) uint8_t Bs[2][kBN * kRowB];
-    __shared__ int jtab[RES ? 2 * kMaxKb : 1];
+__global__ __launch_bounds__(256, DUMP ? 1 : 2) void k_gemm_prefill(GemmArgs a) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint8_t* As = smem;                                                        // [2][128][80]
+    uint8_t* Bs = As + PrefillSmem::a_bytes;                                   // [2][128][144]
+    float* Fs = reinterpret_cast<float*>(Bs + PrefillSmem::b_bytes);           // [2][128]
+    uint8_t* Rf = reinterpret_cast<uint8_t*>(Fs + 2 * kPN);                    // [2][128] residual flags
+    int* tab = reinterpret_cast<int*>(Rf + PrefillSmem::r_bytes);              // [2 block rows][2G]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, kg = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
-    const int tiles_n = (a.N + kBN - 1) / kBN;
-    const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-    const int m0 = tm * kBM, n0 = tn * kBN;
-    const int G = a.K / kGroup, G4 = (G + 3) / 4, nbc = a.K / kBk;
+    const int tiles_n = (a.N + kPN - 1) / kPN;
+    const int m0 = (blockIdx.x / tiles_n) * kPM, n0 = (blockIdx.x % tiles_n) * kPN;
+    const int G = a.K / kGroup, G4 = (G + 3) / 4, nbc = 2 * G;
+    const int br0 = n0 / a.bn;
 
-    // global -> LDS assignment: 512 16-byte chunks per operand tile, two per thread
-    int ld_row[2], ld_part[2];
+    // zipper tables of the tile's block rows (one or two), gathered once
+    if (RES) {
+        for (int i = tid; i < 2 * nbc; i += 256) tab[i] = -1;
+        __syncthreads();
+        zip_table(a, br0, 0, nbc, tab, tid, 256);
+        if ((n0 + kPN - 1) / a.bn != br0 && n0 + 64 < a.N) zip_table(a, br0 + 1, 0, nbc, tab + nbc, tid, 256);
+        __syncthreads();
+    }
+
+    // staging assignment: pieces p = tid and tid + 256 of each tile, row p / 4, 16-byte part p % 4
+    int srow[2], spart[2];
     const uint8_t* ga[2];
     const uint8_t* gb[2];
-    bool va[2], vb[2];
+    int ncol[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int c = tid + 256 * i;
-        ld_row[i] = c >> 2;
-        ld_part[i] = c & 3;
-        const int m = m0 + ld_row[i], nn = n0 + ld_row[i];
-        va[i] = m < a.M;
-        vb[i] = nn < a.N;
-        ga[i] = a.xq + xq_row(0, a.M, va[i] ? m : 0) + ld_part[i] * 16;          // + g * M * 64
-        gb[i] = a.wq + wq_byte(vb[i] ? nn : 0, G, 0, ld_part[i]);                // + g * 1024
+        const int pc = tid + 256 * i;
+        srow[i] = pc >> 2;
+        spart[i] = pc & 3;
+        const int m = min(m0 + srow[i], a.M - 1);        // rows past M read row M-1 (never stored)
+        ncol[i] = min(n0 + srow[i], a.N - 1);             // columns past N likewise
+        ga[i] = a.xq + xq_row(0, a.M, m) + spart[i] * 16;                   // + g * M * 64
+        gb[i] = a.wq + wq_byte(ncol[i], G, 0, spart[i]);                    // + g * 1024
     }
-    const int nw0 = n0 + wn * 64;                 // this wave's first output column
-    const bool wave_cols = nw0 < a.N;
-    const int br = nw0 / a.bn, rbase = nw0 - br * a.bn;
-    const int* tab = jtab + (RES ? wn * kMaxKb : 0);
+    const int fcol = min(n0 + (tid & 127), a.N - 1);     // threads 0-127 stage the factors
 
-    uint4 ra[2], rb[2], rr[4];
-    float sn[4];
-    int rgrp_next = 0;
+    uint4 pa[2], pb[2], pr[2];
+    uint16_t ps = 0;
     auto fetch = [&](int g) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            ra[i] = va[i] ? ldg16(ga[i] + static_cast<int64_t>(g) * a.M * 64) : make_uint4(0, 0, 0, 0);
-            rb[i] = vb[i] ? ldg16(gb[i] + static_cast<int64_t>(g) * 1024) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int nn = nw0 + j * 16 + li;
-            sn[j] = nn < a.N ? f16_bits_to_f32(a.sw[sw_index(nn, G4, g)]) : 0.0f;
-        }
-        if (RES) {
-            const int j0 = wave_cols ? tab[2 * g] : -1, j1 = wave_cols ? tab[2 * g + 1] : -1;
-            rgrp_next = (j0 >= 0) || (j1 >= 0);
-            const int jb = kg < 2 ? j0 : j1;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int nn = nw0 + j * 16 + li;
-                rr[j] = (jb >= 0 && nn < a.N)
-                            ? ldg16(a.rq + (static_cast<int64_t>(jb) * a.bn + rbase + j * 16 + li) * 32 + (kg & 1) * 16)
-                            : make_uint4(0, 0, 0, 0);
+            pa[i] = ldg16(ga[i] + static_cast<int64_t>(g) * a.M * 64);
+            pb[i] = ldg16(gb[i] + static_cast<int64_t>(g) * 1024);
+            pr[i] = make_uint4(0, 0, 0, 0);
+            if (RES) {
+                const int brl = ncol[i] / a.bn - br0;
+                const int j = tab[brl * nbc + 2 * g + (spart[i] >> 1)];
+                if (j >= 0)
+                    pr[i] = ldg16(a.rq + (static_cast<int64_t>(j) * a.bn + ncol[i] % a.bn) * 32 + (spart[i] & 1) * 16);
             }
         }
+        if (tid < kPN) ps = a.sw[sw_index(fcol, G4, g)];
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int g, int buf) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            *reinterpret_cast<uint4*>(&As[buf][ld_row[i] * kRowB + ld_part[i] * 16]) = ra[i];
-            *reinterpret_cast<uint4*>(&Bs[buf][ld_row[i] * kRowB + ld_part[i] * 16]) = rb[i];
+            *reinterpret_cast<uint4*>(As + buf * kPM * kApitch + srow[i] * kApitch + spart[i] * 16) = pa[i];
+            bool res = false;
+            if (RES) {
+                const int brl = ncol[i] / a.bn - br0;
+                res = tab[brl * nbc + 2 * g] >= 0 || tab[brl * nbc + 2 * g + 1] >= 0;
+            }
+            v4i o0, o1;
+            if (res) unpack_comb(pb[i], pr[i], o0, o1);
+            else unpack16(pb[i], o0, o1);
+            uint8_t* d = Bs + buf * kPN * kBpitch + srow[i] * kBpitch + spart[i] * 32;
+            *reinterpret_cast<v4i*>(d) = o0;
+            *reinterpret_cast<v4i*>(d + 16) = o1;
+        }
+        if (tid < kPN) {
+            bool res = false;
+            if (RES) {
+                const int brl = fcol / a.bn - br0;
+                res = tab[brl * nbc + 2 * g] >= 0 || tab[brl * nbc + 2 * g + 1] >= 0;
+            }
+            const float s = f16_bits_to_f32(ps);
+            Fs[buf * kPN + tid] = res ? (s / 14.0f) * 0.0625f : s * 0.00390625f;
+            Rf[buf * kPN + tid] = res;
         }
     };
-
-    if (RES) {
-        for (int i = tid; i < 2 * nbc; i += 256) jtab[(i / nbc) * kMaxKb + i % nbc] = -1;
-        __syncthreads();
-        // both wave columns' block rows (the same row when bn == 128)
-        const int brow0 = n0 / a.bn, brow1 = (n0 + 64) / a.bn;
-        if (n0 < a.N) zip_table(a, brow0, 0, nbc, jtab, tid, 256);
-        if (n0 + 64 < a.N) zip_table(a, brow1, 0, nbc, jtab + kMaxKb, tid, 256);
-        __syncthreads();
-    }
 
     float acc[4][4][4];
 #pragma unroll
@@ -349,61 +374,46 @@ __global__ __launch_bounds__(256, (RES || DUMP) ? 1 : 2) void k_gemm_tiled(GemmA
             for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
 
     fetch(0);
-    stash(0);
-    uint4 rw[4] = {rr[0], rr[1], rr[2], rr[3]};
-    float sc[4] = {sn[0], sn[1], sn[2], sn[3]};
-    int rgrp = rgrp_next;
+    stash(0, 0);
     __syncthreads();
     for (int g = 0; g < G; ++g) {
         const int buf = g & 1;
         if (g + 1 < G) fetch(g + 1);
+        const uint8_t* Ab = As + buf * kPM * kApitch;
+        const uint8_t* Bb = Bs + buf * kPN * kBpitch;
         v4i a0[4], a1[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint4 w = *reinterpret_cast<const uint4*>(&As[buf][(wm * 64 + i * 16 + li) * kRowB + kg * 16]);
+            const uint4 w = *reinterpret_cast<const uint4*>(Ab + (wm * 64 + i * 16 + li) * kApitch + kg * 16);
             unpack16(w, a0[i], a1[i]);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint4 w = *reinterpret_cast<const uint4*>(&Bs[buf][(wn * 64 + j * 16 + li) * kRowB + kg * 16]);
-            v4i b0, b1;
-            float scale;
-            if (RES && rgrp) {
-                unpack_comb(w, rw[j], b0, b1);
-                scale = (sc[j] / 14.0f) * 0.0625f;
-            } else {
-                unpack16(w, b0, b1);
-                scale = sc[j] * 0.00390625f;
-            }
+            const int col = wn * 64 + j * 16 + li;
+            const v4i b0 = *reinterpret_cast<const v4i*>(Bb + col * kBpitch + kg * 32);
+            const v4i b1 = *reinterpret_cast<const v4i*>(Bb + col * kBpitch + kg * 32 + 16);
+            const float f = Fs[buf * kPN + col];
+            const bool rcol = DUMP && Rf[buf * kPN + col];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 v4i c = v4i{0, 0, 0, 0};
                 c = mfma_i8(a0[i], b0, c);
                 c = mfma_i8(a1[i], b1, c);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][j][r] += scale * static_cast<float>(c[r]);
+                for (int r = 0; r < 4; ++r) acc[i][j][r] += f * static_cast<float>(c[r]);
                 if (DUMP) {
-                    const int nn = nw0 + j * 16 + li;
+                    const int nn = n0 + col;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int m = m0 + wm * 64 + i * 16 + kg * 4 + r;
                         if (m < a.M && nn < a.N)
                             a.acc_dump[(static_cast<int64_t>(m) * a.N + nn) * G + g] =
-                                (RES && rgrp) ? (c[r] >> 4) : 14 * (c[r] >> 8);
+                                rcol ? (c[r] >> 4) : 14 * (c[r] >> 8);
                     }
                 }
             }
         }
-        if (g + 1 < G) {
-            stash(buf ^ 1);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sc[j] = sn[j];
-            if (RES) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) rw[j] = rr[j];
-                rgrp = rgrp_next;
-            }
-        }
+        if (g + 1 < G) stash(g + 1, buf ^ 1);
         __syncthreads();
     }
 
@@ -411,7 +421,7 @@ __global__ __launch_bounds__(256, (RES || DUMP) ? 1 : 2) void k_gemm_tiled(GemmA
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int nn = nw0 + j * 16 + li;
+            const int nn = n0 + wn * 64 + j * 16 + li;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + wm * 64 + i * 16 + kg * 4 + r;
@@ -476,9 +486,19 @@ static hipError_t go_decode(const GemmArgs& a, hipStream_t st) {
 }
 
 template <bool RES, bool DUMP, int OUT>
-static hipError_t go_tiled(const GemmArgs& a, hipStream_t st) {
-    const int tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
-    k_gemm_tiled<RES, DUMP, OUT><<<dim3(tiles), dim3(256), 0, st>>>(a);
+static hipError_t go_prefill(const GemmArgs& a, hipStream_t st) {
+    const int tiles = ((a.M + kPM - 1) / kPM) * ((a.N + kPN - 1) / kPN);
+    const size_t lds = PrefillSmem::total(RES, a.K / kGroup);
+    // dynamic LDS above 64 KB needs the kernel's limit raised (once per kernel)
+    static bool raised = false;
+    if (!raised) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_prefill<RES, DUMP, OUT>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(PrefillSmem::total(RES, kMaxGroups)));
+        if (e != hipSuccess) return e;
+        raised = true;
+    }
+    k_gemm_prefill<RES, DUMP, OUT><<<dim3(tiles), dim3(256), lds, st>>>(a);
     return hipGetLastError();
 }
 
@@ -486,7 +506,7 @@ template <bool RES, bool DUMP, int OUT>
 static hipError_t go(const GemmArgs& a, hipStream_t st) {
     if (a.M <= 16) return go_decode<1, RES, DUMP, OUT>(a, st);
     if (a.M <= 32) return go_decode<2, RES, DUMP, OUT>(a, st);
-    return go_tiled<RES, DUMP, OUT>(a, st);
+    return go_prefill<RES, DUMP, OUT>(a, st);
 }
 
 // ---------------------------------------------------------------------------
