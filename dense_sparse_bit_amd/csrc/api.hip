@@ -100,7 +100,7 @@ int mq_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* x
     if (M < 0 || K <= 0 || (K & 1) || bad_dtype(x_dtype)) return MQ_ERR_INVALID_ARG;
     if (K % mq::kGroup || M > (int64_t(1) << 31) - 1 || M * K > (int64_t(1) << 40)) return MQ_ERR_UNSUPPORTED;
     if (M == 0) return MQ_OK;
-    if (!x || !xq || !sx) return MQ_ERR_INVALID_ARG;
+    if (!x || !xq || !sx || !aligned16(x) || !aligned16(xq)) return MQ_ERR_INVALID_ARG;
     return hip_status(mq::launch_quant_act(x, x_dtype == MQ_BF16, M, K, xq, sx, static_cast<hipStream_t>(stream)));
 }
 

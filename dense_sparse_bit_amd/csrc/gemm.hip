@@ -132,6 +132,9 @@ __device__ __forceinline__ void dec_fetch_res(DecStep<MT, QS>& st, const GemmArg
     }
 }
 
+// One fp8 MFMA per group and row tile gives P * 2^-18 exactly; a group with a
+// chosen block in this block row adds the residual product Pr the same way and
+// forms T = 14 P + Pr (exact in fp32), dequantized with s_r = fp32(s / 14).
 template <int MT, int QS, bool RES, bool DUMP>
 __device__ __forceinline__ void dec_compute(const DecStep<MT, QS>& st, const GemmArgs& a, int n, int G, int g0,
                                             int lane, float (&acc)[MT][4]) {
@@ -142,30 +145,39 @@ __device__ __forceinline__ void dec_compute(const DecStep<MT, QS>& st, const Gem
         if (g >= G) break;
         const float sc = f16_bits_to_f32(static_cast<uint16_t>(st.s[u >> 1] >> (16 * (u & 1))));
         const bool res = RES && ((st.rg >> u) & 1);
-        v4i b0, b1;
-        float scale;
+        const v8i b = f8_operand(st.w[u]);
         if (res) {
-            unpack_comb(st.w[u], st.r[u], b0, b1);
-            scale = (sc / 14.0f) * 0.0625f;
-        } else {
-            unpack16(st.w[u], b0, b1);
-            scale = sc * 0.00390625f;
-        }
+            const v8i rb = f8_operand(st.r[u]);
+            const float fr = (sc / 14.0f) * kF8Unit;
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            v4i a0, a1;
-            unpack16(st.x[t][u], a0, a1);
-            v4i c = v4i{0, 0, 0, 0};
-            c = mfma_i8(a0, b0, c);
-            c = mfma_i8(a1, b1, c);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[t][r] += scale * static_cast<float>(c[r]);
-            if (DUMP) {
+            for (int t = 0; t < MT; ++t) {
+                const v8i av = f8_operand(st.x[t][u]);
+                const v4f p = mfma_f8(av, b, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                const v4f pr = mfma_f8(av, rb, v4f{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int m = t * 16 + kg * 4 + r;
-                    if (m < a.M)
-                        a.acc_dump[(static_cast<int64_t>(m) * a.N + n) * G + g] = res ? (c[r] >> 4) : 14 * (c[r] >> 8);
+                    const float tt = fmaf(14.0f, p[r], pr[r]);
+                    acc[t][r] = fmaf(fr, tt, acc[t][r]);
+                    if (DUMP) {
+                        const int m = t * 16 + kg * 4 + r;
+                        if (m < a.M)
+                            a.acc_dump[(static_cast<int64_t>(m) * a.N + n) * G + g] = static_cast<int>(tt * kF8Unit);
+                    }
+                }
+            }
+        } else {
+            const float f = sc * kF8Unit;
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const v4f p = mfma_f8(f8_operand(st.x[t][u]), b, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    acc[t][r] = fmaf(f, p[r], acc[t][r]);
+                    if (DUMP) {
+                        const int m = t * 16 + kg * 4 + r;
+                        if (m < a.M)
+                            a.acc_dump[(static_cast<int64_t>(m) * a.N + n) * G + g] = 14 * static_cast<int>(p[r] * kF8Unit);
+                    }
                 }
             }
         }
@@ -252,40 +264,33 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
 
 // ===========================================================================
 // Prefill kernel, M > 32: 128 x 128 output tile per workgroup, four waves of
-// 64 x 64, one K group per step, two LDS stages.
-//   * The weight tile is staged in LDS as int8 MFMA operands: the staging
-//     threads widen each 16-byte nibble piece once per workgroup, to 16 q for
-//     plain groups or to 14 q + r where the row's block is a chosen residual
-//     block (its residual row is fetched with the base piece). The zipper walk
-//     thus happens at staging; the waves' MFMA loop is the same with or without
-//     residual blocks.
-//   * Each column's dequantization factor for the group (s/256, or s_r/16 in a
-//     residual group) is staged beside the tile.
-//   * The activation tile stays as nibbles in LDS (half the bytes the waves read)
-//     and is widened in registers.
-//   * Global loads of group g+1 are issued before group g's MFMAs and written to
-//     the other LDS stage after them: one barrier per group.
+// 64 x 64, one K group (one fp8 MFMA deep) per step, two LDS stages.
+//   * Operand tiles move from memory to LDS without passing through registers
+//     (global_load_lds, 16 bytes per lane): each 16-row subtile of a group is one
+//     1 KB load, placed in LDS in MFMA lane order (lane 16 kc + r holds row r,
+//     codes 32 kc .. 32 kc + 31). The packed weight tiles already have that
+//     order; activation rows are gathered into it. No staging registers, no LDS
+//     store instructions, half the LDS bytes of fp8 operands, and every LDS read
+//     is one conflict-free 1 KB access.
+//   * Each wave widens its operands to fp8 after its LDS read (three operations
+//     per 8 codes) and dequantizes each group's exact products with the
+//     column's factor s * 2^18 (or fp32(s / 14) * 2^18 in a residual group).
+//   * Residual blocks: a wave's 64 columns lie in one block row, so whether a
+//     group holds a chosen block is the same for the whole wave (a scalar
+//     branch). Such a group takes a second MFMA per subtile on the residual
+//     codes, which the wave loads from memory one group ahead (zero for a
+//     half-group without a chosen block); the MFMA accumulates them onto 14 P,
+//     giving T = 14 P + Pr exactly, before the dequant.
+//   * The loads of group g+1 are issued right after group g's LDS reads and
+//     complete during its MFMAs: one wait and one barrier per group.
 // ===========================================================================
 constexpr int kPM = 128, kPN = 128;
-constexpr int kApitch = 80;        // LDS bytes per activation row: 64 nibble bytes + 16 pad
-constexpr int kBpitch = 144;       // LDS bytes per weight row: 128 int8 operand bytes + 16 pad
-
-struct PrefillSmem {
-    static constexpr size_t a_bytes = 2 * kPM * kApitch;
-    static constexpr size_t b_bytes = 2 * kPN * kBpitch;
-    static constexpr size_t f_bytes = 2 * kPN * sizeof(float);
-    static constexpr size_t r_bytes = 2 * kPN;
-    static size_t total(bool res, int G) { return a_bytes + b_bytes + f_bytes + r_bytes + (res ? 2 * 2 * G * sizeof(int) : 0); }
-};
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <bool RES, bool DUMP, int OUTMODE>
 __global__ __launch_bounds__(256, DUMP ? 1 : 2) void k_gemm_prefill(GemmArgs a) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    uint8_t* As = smem;                                                        // [2][128][80]
-    uint8_t* Bs = As + PrefillSmem::a_bytes;                                   // [2][128][144]
-    float* Fs = reinterpret_cast<float*>(Bs + PrefillSmem::b_bytes);           // [2][128]
-    uint8_t* Rf = reinterpret_cast<uint8_t*>(Fs + 2 * kPN);                    // [2][128] residual flags
-    int* tab = reinterpret_cast<int*>(Rf + PrefillSmem::r_bytes);              // [2 block rows][2G]
+    __shared__ __align__(16) uint8_t tiles[2][2][8][1024];          // [stage][A, B][subtile][lane * 16]
+    __shared__ int tab[RES ? 2 * 2 * kMaxGroups : 1];                // [2 block rows][2G]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, kg = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
@@ -303,66 +308,72 @@ __global__ __launch_bounds__(256, DUMP ? 1 : 2) void k_gemm_prefill(GemmArgs a) 
         __syncthreads();
     }
 
-    // staging assignment: pieces p = tid and tid + 256 of each tile, row p / 4, 16-byte part p % 4
-    int srow[2], spart[2];
-    const uint8_t* ga[2];
-    const uint8_t* gb[2];
-    int ncol[2];
+    // Loads go through buffer resources with a per-group base: 32-bit lane offsets
+    // stay small, and rows past M or subtiles past N fall outside the range and
+    // read zero (their outputs are never stored). Wave w loads subtiles 2w and
+    // 2w+1 of both operands.
+    const int nsub = min(a.N / 16 - n0 / 16, 8);                    // column subtiles of this tile
+    const uint32_t a_range = static_cast<uint32_t>(min(a.M - m0, kPM)) * 64u;
+    const uint32_t b_range = static_cast<uint32_t>(nsub - 1) * static_cast<uint32_t>(G) * 1024u + 1024u;
+    uint32_t aoff[2], boff[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int pc = tid + 256 * i;
-        srow[i] = pc >> 2;
-        spart[i] = pc & 3;
-        const int m = min(m0 + srow[i], a.M - 1);        // rows past M read row M-1 (never stored)
-        ncol[i] = min(n0 + srow[i], a.N - 1);             // columns past N likewise
-        ga[i] = a.xq + xq_row(0, a.M, m) + spart[i] * 16;                   // + g * M * 64
-        gb[i] = a.wq + wq_byte(ncol[i], G, 0, spart[i]);                    // + g * 1024
+    for (int u = 0; u < 2; ++u) {
+        const int st = 2 * wave + u;
+        aoff[u] = static_cast<uint32_t>(16 * st + li) * 64u + kg * 16u;
+        boff[u] = static_cast<uint32_t>(st) * static_cast<uint32_t>(G) * 1024u + lane * 16u;
     }
-    const int fcol = min(n0 + (tid & 127), a.N - 1);     // threads 0-127 stage the factors
-
-    uint4 pa[2], pb[2], pr[2];
-    uint16_t ps = 0;
-    auto fetch = [&](int g) {
+    auto issue = [&](int g, int stage) {
+        const __amdgpu_buffer_rsrc_t ra = buf_rsrc(a.xq + (static_cast<int64_t>(g) * a.M + m0) * 64, a_range);
+        const __amdgpu_buffer_rsrc_t rb = buf_rsrc(a.wq + wq_tile(n0 >> 4, G, g), b_range);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            pa[i] = ldg16(ga[i] + static_cast<int64_t>(g) * a.M * 64);
-            pb[i] = ldg16(gb[i] + static_cast<int64_t>(g) * 1024);
-            pr[i] = make_uint4(0, 0, 0, 0);
-            if (RES) {
-                const int brl = ncol[i] / a.bn - br0;
-                const int j = tab[brl * nbc + 2 * g + (spart[i] >> 1)];
-                if (j >= 0)
-                    pr[i] = ldg16(a.rq + (static_cast<int64_t>(j) * a.bn + ncol[i] % a.bn) * 32 + (spart[i] & 1) * 16);
-            }
+        for (int u = 0; u < 2; ++u) {
+            const int st = 2 * wave + u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)&tiles[stage][0][st][0], 16, aoff[u], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)&tiles[stage][1][st][0], 16, boff[u], 0, 0, 0);
         }
-        if (tid < kPN) ps = a.sw[sw_index(fcol, G4, g)];
     };
-    auto stash = [&](int g, int buf) {
+    // the lane's four column scales of group g: one 16-bit load each
+    const __amdgpu_buffer_rsrc_t rs =
+        buf_rsrc(a.sw + static_cast<int64_t>(n0 >> 4) * G4 * 64, static_cast<uint32_t>(nsub) * static_cast<uint32_t>(G4) * 128u);
+    const uint32_t soff = (static_cast<uint32_t>(wn * 4) * static_cast<uint32_t>(G4) * 64u + li * 4u) * 2u;
+    auto scales = [&](int g, uint16_t (&sc)[4]) {
+        const int gs = ((g >> 2) * 64 + (g & 3)) * 2;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            *reinterpret_cast<uint4*>(As + buf * kPM * kApitch + srow[i] * kApitch + spart[i] * 16) = pa[i];
-            bool res = false;
-            if (RES) {
-                const int brl = ncol[i] / a.bn - br0;
-                res = tab[brl * nbc + 2 * g] >= 0 || tab[brl * nbc + 2 * g + 1] >= 0;
-            }
-            v4i o0, o1;
-            if (res) unpack_comb(pb[i], pr[i], o0, o1);
-            else unpack16(pb[i], o0, o1);
-            uint8_t* d = Bs + buf * kPN * kBpitch + srow[i] * kBpitch + spart[i] * 32;
-            *reinterpret_cast<v4i*>(d) = o0;
-            *reinterpret_cast<v4i*>(d + 16) = o1;
+        for (int j = 0; j < 4; ++j)
+            sc[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff + static_cast<uint32_t>(j) * static_cast<uint32_t>(G4) * 128u, gs, 0);
+    };
+
+    // this wave's residual payload: its 64 columns' block row, as a buffer range
+    // (offsets past it read zero), and the lane's row in it for column subtile j
+    __amdgpu_buffer_rsrc_t rsrc = buf_rsrc(a.wq, 0u);
+    int wtab = 0, wlo = 0;
+    uint32_t rrow0 = 0;
+    if (RES) {
+        const int wc0 = n0 + wn * 64;
+        if (wc0 < a.N) {
+            const int brw = wc0 / a.bn;
+            wtab = (brw - br0) * nbc;
+            wlo = clampi(a.row_ptr[brw], 0, a.nnz);
+            const int whi = clampi(a.row_ptr[brw + 1], wlo, a.nnz);
+            rsrc = buf_rsrc(whi > wlo ? a.rq + static_cast<int64_t>(wlo) * a.bn * 32 : a.wq,
+                            static_cast<uint32_t>(whi - wlo) * static_cast<uint32_t>(a.bn) * 32u);
         }
-        if (tid < kPN) {
-            bool res = false;
-            if (RES) {
-                const int brl = fcol / a.bn - br0;
-                res = tab[brl * nbc + 2 * g] >= 0 || tab[brl * nbc + 2 * g + 1] >= 0;
-            }
-            const float s = f16_bits_to_f32(ps);
-            Fs[buf * kPN + tid] = res ? (s / 14.0f) * 0.0625f : s * 0.00390625f;
-            Rf[buf * kPN + tid] = res;
+        rrow0 = static_cast<uint32_t>((wc0 + li) % a.bn);
+    }
+    // residual codes of group g for this wave's columns; returns whether the wave
+    // has a chosen block in the group (the same in every lane)
+    auto fetch_res = [&](int g, uint4 (&rr)[4]) -> bool {
+        const int j0 = __builtin_amdgcn_readfirstlane(tab[wtab + 2 * g]);
+        const int j1 = __builtin_amdgcn_readfirstlane(tab[wtab + 2 * g + 1]);
+        if (j0 < 0 && j1 < 0) return false;
+        const int jb = kg < 2 ? j0 : j1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t off = jb >= 0 ? ((jb - wlo) * static_cast<uint32_t>(a.bn) + rrow0 + 16 * j) * 32u + (kg & 1) * 16u
+                                         : 0xFFFFFFF0u;
+            rr[j] = buf_load16(rsrc, off);
         }
+        return true;
     };
 
     float acc[4][4][4];
@@ -372,49 +383,81 @@ __global__ __launch_bounds__(256, DUMP ? 1 : 2) void k_gemm_prefill(GemmArgs a) 
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+    auto dump = [&](int g, int i, int j, int r, int T) {
+        const int m = m0 + wm * 64 + i * 16 + kg * 4 + r;
+        const int nn = n0 + wn * 64 + j * 16 + li;
+        if (m < a.M && nn < a.N) a.acc_dump[(static_cast<int64_t>(m) * a.N + nn) * G + g] = T;
+    };
 
-    fetch(0);
-    stash(0, 0);
+    uint16_t sc[4];
+    uint4 rr[4];
+    bool res_cur = false;
+    issue(0, 0);
+    scales(0, sc);
+    if (RES) res_cur = fetch_res(0, rr);
+    __builtin_amdgcn_s_waitcnt(0);   // all counters: the direct loads are not tracked by the barrier's fence
     __syncthreads();
     for (int g = 0; g < G; ++g) {
-        const int buf = g & 1;
-        if (g + 1 < G) fetch(g + 1);
-        const uint8_t* Ab = As + buf * kPM * kApitch;
-        const uint8_t* Bb = Bs + buf * kPN * kBpitch;
-        v4i a0[4], a1[4];
+        const int stage = g & 1;
+        uint4 araw[4], braw[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint4 w = *reinterpret_cast<const uint4*>(Ab + (wm * 64 + i * 16 + li) * kApitch + kg * 16);
-            unpack16(w, a0[i], a1[i]);
-        }
+        for (int i = 0; i < 4; ++i) araw[i] = *reinterpret_cast<const uint4*>(&tiles[stage][0][wm * 4 + i][lane * 16]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) braw[j] = *reinterpret_cast<const uint4*>(&tiles[stage][1][wn * 4 + j][lane * 16]);
+        const bool res = RES && res_cur;
+        float f[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int col = wn * 64 + j * 16 + li;
-            const v4i b0 = *reinterpret_cast<const v4i*>(Bb + col * kBpitch + kg * 32);
-            const v4i b1 = *reinterpret_cast<const v4i*>(Bb + col * kBpitch + kg * 32 + 16);
-            const float f = Fs[buf * kPN + col];
-            const bool rcol = DUMP && Rf[buf * kPN + col];
+            const float s = f16_bits_to_f32(sc[j]);
+            f[j] = res ? (s / 14.0f) * kF8Unit : s * kF8Unit;
+        }
+        // the next group's loads (the last step re-loads group G-1 into the idle stage)
+        const int gn = min(g + 1, G - 1);
+        issue(gn, stage ^ 1);
+        scales(gn, sc);
+        // next group's residual codes: now if this group does not use the
+        // registers, else after its residual MFMAs
+        bool res_next = false;
+        if (RES && !res && g + 1 < G) res_next = fetch_res(g + 1, rr);
+        v8i av[4], bv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v4i c = v4i{0, 0, 0, 0};
-                c = mfma_i8(a0[i], b0, c);
-                c = mfma_i8(a1[i], b1, c);
+        for (int i = 0; i < 4; ++i) av[i] = f8_operand(araw[i]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[i][j][r] += f * static_cast<float>(c[r]);
-                if (DUMP) {
-                    const int nn = n0 + col;
+        for (int j = 0; j < 4; ++j) bv[j] = f8_operand(braw[j]);
+        if (res) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const v8i rv = f8_operand(rr[j]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v4f p = mfma_f8(av[i], bv[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                    // T = 14 P + Pr: the residual MFMA accumulates onto 14 P (exact:
+                    // every partial sum is a multiple of 2^-18 far below 2^6)
+                    const v4f t = mfma_f8(av[i], rv, p * 14.0f);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int m = m0 + wm * 64 + i * 16 + kg * 4 + r;
-                        if (m < a.M && nn < a.N)
-                            a.acc_dump[(static_cast<int64_t>(m) * a.N + nn) * G + g] =
-                                rcol ? (c[r] >> 4) : 14 * (c[r] >> 8);
+                        acc[i][j][r] = fmaf(f[j], t[r], acc[i][j][r]);
+                        if (DUMP) dump(g, i, j, r, static_cast<int>(t[r] * kF8Unit));
                     }
                 }
             }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const v4f p = mfma_f8(av[i], bv[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        acc[i][j][r] = fmaf(f[j], p[r], acc[i][j][r]);
+                        if (DUMP) dump(g, i, j, r, 14 * static_cast<int>(p[r] * kF8Unit));
+                    }
+                }
         }
-        if (g + 1 < G) stash(g + 1, buf ^ 1);
+        if (RES && res && g + 1 < G) res_next = fetch_res(g + 1, rr);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        res_cur = res_next;
     }
 
 #pragma unroll
@@ -455,12 +498,14 @@ __global__ __launch_bounds__(256) void k_residual_merge(GemmArgs a) {
             if (ma < a.M) av = *reinterpret_cast<const uint2*>(a.xq + xq_row(g, a.M, ma) + (kb & 1) * 32 + kg * 8);
             const uint2 rv =
                 *reinterpret_cast<const uint2*>(a.rq + (static_cast<int64_t>(p) * a.bn + rrow) * 32 + kg * 8);
-            const v4i aop = v4i{(int)nib16_even(av.x), (int)nib16_odd(av.x), (int)nib16_even(av.y), (int)nib16_odd(av.y)};
-            const v4i bop = v4i{(int)nib16_even(rv.x), (int)nib16_odd(rv.x), (int)nib16_even(rv.y), (int)nib16_odd(rv.y)};
-            const v4i c = mfma_i8(aop, bop, v4i{0, 0, 0, 0});
+            // a block is 64 inputs: each lane's 16 codes fill half of the fp8
+            // operand, the other half is zero in both operands
+            const v8i aop = v8i{(int)f8_even(av.x), (int)f8_odd(av.x), (int)f8_even(av.y), (int)f8_odd(av.y), 0, 0, 0, 0};
+            const v8i bop = v8i{(int)f8_even(rv.x), (int)f8_odd(rv.x), (int)f8_even(rv.y), (int)f8_odd(rv.y), 0, 0, 0, 0};
+            const v4f c = mfma_f8(aop, bop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
             const float sr = f16_bits_to_f32(a.sw[sw_index(n, G4, g)]) / 14.0f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] += (sr * 0.00390625f) * static_cast<float>(c[r]);
+            for (int r = 0; r < 4; ++r) acc[r] = fmaf(sr * kF8Unit, c[r], acc[r]);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -488,17 +533,7 @@ static hipError_t go_decode(const GemmArgs& a, hipStream_t st) {
 template <bool RES, bool DUMP, int OUT>
 static hipError_t go_prefill(const GemmArgs& a, hipStream_t st) {
     const int tiles = ((a.M + kPM - 1) / kPM) * ((a.N + kPN - 1) / kPN);
-    const size_t lds = PrefillSmem::total(RES, a.K / kGroup);
-    // dynamic LDS above 64 KB needs the kernel's limit raised (once per kernel)
-    static bool raised = false;
-    if (!raised) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_prefill<RES, DUMP, OUT>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 static_cast<int>(PrefillSmem::total(RES, kMaxGroups)));
-        if (e != hipSuccess) return e;
-        raised = true;
-    }
-    k_gemm_prefill<RES, DUMP, OUT><<<dim3(tiles), dim3(256), lds, st>>>(a);
+    k_gemm_prefill<RES, DUMP, OUT><<<dim3(tiles), dim3(256), 0, st>>>(a);
     return hipGetLastError();
 }
 

@@ -124,43 +124,48 @@ __device__ __forceinline__ bool fast_ok(const GroupScale& g) {
     return fabsf(g.rs) <= 3.0e38f && fabsf(g.rsr) <= 3.0e38f;
 }
 
-// ---- int4 -> int8 operand construction for the int8 MFMA ------------------
-// A 32-bit word holds 8 two's-complement nibbles (k0 in bits 0-3). Placing a
-// nibble in the high half of a byte gives the int8 value 16*v, so two masks
-// turn 8 nibbles into 8 int8 operands (k even in one dword, k odd in the other);
-// the same permutation of k is applied to both MFMA operands, which leaves the
-// dot product unchanged.
-__device__ __forceinline__ uint32_t nib16_even(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
-__device__ __forceinline__ uint32_t nib16_odd(uint32_t w) { return w & 0xF0F0F0F0u; }
+// ---- packed int4 codes and the fp8 MFMA -----------------------------------
+// gfx950 has no int4 MFMA, and the int8 one returns integers that need a
+// conversion per output before the per-group scale applies. The fp8 (e4m3)
+// MFMA v_mfma_f32_16x16x128_f8f6f4 covers a whole 128-input group in one
+// instruction at the int8 rate and returns fp32 directly. A code c in [-7, 7]
+// is the e4m3 subnormal with sign bit 7 and mantissa |c| (value c * 2^-9), so
+// each product is an exact multiple of 2^-18 and every group sum (at most
+// 128 * 49 units) is exact in fp32: the MFMA result is the exact integer dot
+// product times 2^-18.
+//
+// The packed code word is chosen so that two masks make those bytes: a 32-bit
+// word holds 8 consecutive codes c0..c7; nibble e (bits 4e..4e+3) holds |c_e|
+// in its low three bits and, in its high bit, the sign of code (e - 1) mod 8.
+// Then  word & 0x87878787  is the e4m3 bytes of c0, c2, c4, c6 and
+// rotr(word, 4) & 0x87878787  those of c1, c3, c5, c7. The same k order is used
+// for both MFMA operands, which leaves the dot product unchanged.
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
-// 16 bytes of nibbles (32 values) -> two MFMA operands of 16 int8 (values x16).
-__device__ __forceinline__ void unpack16(const uint4 w, v4i& op0, v4i& op1) {
-    op0 = v4i{(int)nib16_even(w.x), (int)nib16_odd(w.x), (int)nib16_even(w.y), (int)nib16_odd(w.y)};
-    op1 = v4i{(int)nib16_even(w.z), (int)nib16_odd(w.z), (int)nib16_even(w.w), (int)nib16_odd(w.w)};
-}
+constexpr float kF8Unit = 262144.0f;   // 2^18: an MFMA result of 1.0 is 2^18 code products
 
-// Combined operand 14*q + r per byte (plain int8, |value| <= 105), from the base
-// word wq and residual word wr. In offset form q' = q+8, r' = r+8 (nibble ^ 8)
-// every byte of 14*q' + r' + 8 stays in [23, 233], so whole-word integer
-// arithmetic produces each byte without carries; xor 0x80 then subtracts 128.
-__device__ __forceinline__ uint32_t comb_even(uint32_t qo, uint32_t ro) {
-    const uint32_t qe = qo & 0x0F0F0F0Fu, re = ro & 0x0F0F0F0Fu;
-    return (((qe << 4) - (qe << 1)) + re + 0x08080808u) ^ 0x80808080u;
-}
-__device__ __forceinline__ uint32_t comb_odd(uint32_t qo, uint32_t ro) {
-    const uint32_t q16 = qo & 0xF0F0F0F0u, rd = (ro >> 4) & 0x0F0F0F0Fu;
-    return ((q16 - (q16 >> 3)) + rd + 0x08080808u) ^ 0x80808080u;
-}
-__device__ __forceinline__ void unpack_comb(const uint4 wq, const uint4 wr, v4i& op0, v4i& op1) {
-    const uint32_t x = 0x88888888u;
-    const uint32_t q0 = wq.x ^ x, q1 = wq.y ^ x, q2 = wq.z ^ x, q3 = wq.w ^ x;
-    const uint32_t r0 = wr.x ^ x, r1 = wr.y ^ x, r2 = wr.z ^ x, r3 = wr.w ^ x;
-    op0 = v4i{(int)comb_even(q0, r0), (int)comb_odd(q0, r0), (int)comb_even(q1, r1), (int)comb_odd(q1, r1)};
-    op1 = v4i{(int)comb_even(q2, r2), (int)comb_odd(q2, r2), (int)comb_even(q3, r3), (int)comb_odd(q3, r3)};
+__device__ __forceinline__ uint32_t f8_even(uint32_t w) { return w & 0x87878787u; }
+__device__ __forceinline__ uint32_t f8_odd(uint32_t w) { return __builtin_rotateright32(w, 4) & 0x87878787u; }
+
+// 16 packed bytes (32 codes) -> one fp8 MFMA operand
+__device__ __forceinline__ v8i f8_operand(const uint4 w) {
+    return v8i{(int)f8_even(w.x), (int)f8_odd(w.x), (int)f8_even(w.y), (int)f8_odd(w.y),
+               (int)f8_even(w.z), (int)f8_odd(w.z), (int)f8_even(w.w), (int)f8_odd(w.w)};
 }
 
-__device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
-    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+// 8 two's-complement nibbles (code e in bits 4e..4e+3) -> the packed code word:
+// sign bits s (bit 4e), magnitudes by a per-nibble negate (c ^ 15) + 1, and the
+// signs rotated by 7 bits into the spare high bit of the next nibble
+__device__ __forceinline__ uint32_t code_word(uint32_t t) {
+    const uint32_t sgn = (t >> 3) & 0x11111111u;
+    const uint32_t mag = (t ^ ((sgn << 4) - sgn)) + sgn;
+    return mag | __builtin_rotateleft32(sgn, 7);
+}
+
+__device__ __forceinline__ v4f mfma_f8(v8i a, v8i b, v4f c) {
+    // format selectors 0/0 (e4m3 both operands), no block scales
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) {

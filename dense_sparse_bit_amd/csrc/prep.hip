@@ -64,39 +64,57 @@ __global__ __launch_bounds__(256) void k_hessian(const void* __restrict__ x, int
 
 // ---------------------------------------------------------------------------
 // a4: per-token symmetric int4 quantization. One workgroup per token; each
-// thread keeps its pairs of values in registers between the exact max-reduction
-// of |x| (order-free) and the quantization, so x is read once. Codes are stored
-// group-major ([K/128][M][64 B]), the layout the GEMM loads from.
+// thread owns code words (8 consecutive inputs each) and keeps their values in
+// registers between the exact max-reduction of |x| (order-free) and the
+// quantization, so x is read once. Words are stored group-major
+// ([K/128][M][64 B]), the layout the GEMM loads from.
 // ---------------------------------------------------------------------------
-constexpr int kQaRegs = 16;     // pairs kept in registers per thread (K <= 8192 read once)
+constexpr int kQaWords = 4;     // words kept in registers per thread (K <= 8192 read once)
 
-__device__ __forceinline__ float2 load_pair(const void* x, bool bf16, int64_t j) {
+__device__ __forceinline__ void load8(const void* row, bool bf16, int64_t j, float (&v)[8]) {
     if (bf16) {
-        const uint32_t u = static_cast<const uint32_t*>(x)[j];
-        return make_float2(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+        const uint4 u = static_cast<const uint4*>(row)[j];
+        const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(p[i] << 16);
+            v[2 * i + 1] = __uint_as_float(p[i] & 0xffff0000u);
+        }
+    } else {
+        const float4 a = static_cast<const float4*>(row)[2 * j];
+        const float4 b = static_cast<const float4*>(row)[2 * j + 1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
-    return static_cast<const float2*>(x)[j];
 }
 
 __global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, int bf16, int64_t M, int64_t K,
                                                    uint8_t* __restrict__ xq, float* __restrict__ sx) {
-    const int64_t m = blockIdx.x, P = K / 2;
+    const int64_t m = blockIdx.x, W = K / 8;
     const void* row = bf16 ? static_cast<const void*>(static_cast<const uint16_t*>(x) + m * K)
                            : static_cast<const void*>(static_cast<const float*>(x) + m * K);
     const int t = threadIdx.x;
     __shared__ float red[4];
-    __shared__ uint8_t fixb[4][kQaRegs];       // per-wave code bytes of a repaired lane
-    float2 v[kQaRegs];
+    __shared__ uint8_t fixb[4][8 * kQaWords];   // per-wave codes of a repaired lane
+    float v[kQaWords][8];
     float a = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kQaRegs; ++i) {
+    for (int i = 0; i < kQaWords; ++i) {
         const int64_t j = t + 256 * i;
-        v[i] = j < P ? load_pair(row, bf16, j) : make_float2(0.0f, 0.0f);
-        a = fmaxf(a, fmaxf(fabsf(v[i].x), fabsf(v[i].y)));
+        if (j < W) {
+            load8(row, bf16, j, v[i]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[i][e]));
     }
-    for (int64_t j = t + 256 * kQaRegs; j < P; j += 256) {
-        const float2 u = load_pair(row, bf16, j);
-        a = fmaxf(a, fmaxf(fabsf(u.x), fabsf(u.y)));
+    for (int64_t j = t + 256 * kQaWords; j < W; j += 256) {
+        float u[8];
+        load8(row, bf16, j, u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(u[e]));
     }
     for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
     if ((t & 63) == 0) red[t >> 6] = a;
@@ -105,58 +123,61 @@ __global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, i
     const float s = a / 7.0f;
     const float rs = s == 0.0f ? 0.0f : 1.0f / s;
     if (t == 0) sx[m] = s;
-    // group-major output: byte j of the row (inputs 2j, 2j+1) goes to group j/64
-    auto code = [&](float v) { return static_cast<int>(rtn_codef(v, s, rs)) & 15; };
-    auto dst = [&](int64_t j) { return xq + xq_row(j >> 6, M, m) + (j & 63); };
+    // group-major output: word j (inputs 8j..8j+7) is bytes 4(j%16).. of group j/16's chunk
+    auto dst = [&](int64_t j) { return reinterpret_cast<uint32_t*>(xq + xq_row(j >> 4, M, m) + (j & 15) * 4); };
     // branch-free codes for the values held in registers; rare near-ties (or a
     // non-finite reciprocal) redo them with the exact quantizer
-    static_assert(kQaRegs == 16, "four code bytes per word, four words");
-    uint32_t wd[4] = {0, 0, 0, 0};
+    uint32_t nib[kQaWords];
     float worst = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kQaRegs; ++i) {
-        const uint32_t c = (static_cast<uint32_t>(static_cast<int>(rtn_fast(v[i].x, rs, worst))) & 15u) |
-                           ((static_cast<uint32_t>(static_cast<int>(rtn_fast(v[i].y, rs, worst))) & 15u) << 4);
-        wd[i >> 2] |= c << (8 * (i & 3));
+    for (int i = 0; i < kQaWords; ++i) {
+        nib[i] = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            nib[i] |= (static_cast<uint32_t>(static_cast<int>(rtn_fast(v[i][e], rs, worst))) & 15u) << (4 * e);
     }
-    uint4 bytes = make_uint4(wd[0], wd[1], wd[2], wd[3]);
     const bool redo = !(worst < kFastMargin) || !(fabsf(rs) <= 3.0e38f);
     // Rare: a quotient within 4e-6 of a rounding boundary. The wave repairs each
-    // flagged lane L together: lane i < 16 recodes L's pair i exactly, and L
-    // gathers the bytes through LDS.
+    // flagged lane L together: lane i < 32 recodes L's value i exactly, and L
+    // gathers the codes through LDS.
     uint64_t flagged = __ballot(redo);
     while (flagged) {
         const int L = __builtin_ctzll(flagged);
         flagged &= flagged - 1;
-        const int tL = (t & ~63) + L;
-        if ((t & 63) < kQaRegs) {
-            const int64_t j = tL + 256 * (t & 63);
+        const int tL = (t & ~63) + L, l = t & 63;
+        if (l < 8 * kQaWords) {
+            const int64_t j = tL + 256 * (l >> 3);
             uint8_t c = 0;
-            if (j < P) {
-                const float2 u = load_pair(row, bf16, j);
-                c = static_cast<uint8_t>((static_cast<int>(rtn_codef(u.x, s, rs)) & 15) |
-                                         ((static_cast<int>(rtn_codef(u.y, s, rs)) & 15) << 4));
+            if (j < W) {
+                float u[8];
+                load8(row, bf16, j, u);
+                c = static_cast<uint8_t>(static_cast<int>(rtn_codef(u[l & 7], s, rs)) & 15);
             }
-            fixb[t >> 6][t & 63] = c;
+            fixb[t >> 6][l] = c;
         }
         __builtin_amdgcn_wave_barrier();
-        if ((t & 63) == L) {
-            uint32_t f[4] = {0, 0, 0, 0};
+        if (l == L) {
 #pragma unroll
-            for (int i = 0; i < kQaRegs; ++i) f[i >> 2] |= static_cast<uint32_t>(fixb[t >> 6][i]) << (8 * (i & 3));
-            bytes = make_uint4(f[0], f[1], f[2], f[3]);
+            for (int i = 0; i < kQaWords; ++i) {
+                nib[i] = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) nib[i] |= static_cast<uint32_t>(fixb[t >> 6][8 * i + e]) << (4 * e);
+            }
         }
         __builtin_amdgcn_wave_barrier();
     }
-    const uint32_t bw[4] = {bytes.x, bytes.y, bytes.z, bytes.w};
 #pragma unroll
-    for (int i = 0; i < kQaRegs; ++i) {
+    for (int i = 0; i < kQaWords; ++i) {
         const int64_t j = t + 256 * i;
-        if (j < P) *dst(j) = static_cast<uint8_t>(bw[i >> 2] >> (8 * (i & 3)));
+        if (j < W) *dst(j) = code_word(nib[i]);
     }
-    for (int64_t j = t + 256 * kQaRegs; j < P; j += 256) {
-        const float2 u = load_pair(row, bf16, j);
-        *dst(j) = static_cast<uint8_t>(code(u.x) | (code(u.y) << 4));
+    for (int64_t j = t + 256 * kQaWords; j < W; j += 256) {
+        float u[8];
+        load8(row, bf16, j, u);
+        uint32_t n8 = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) n8 |= (static_cast<uint32_t>(static_cast<int>(rtn_codef(u[e], s, rs))) & 15u) << (4 * e);
+        *dst(j) = code_word(n8);
     }
 }
 
@@ -416,6 +437,7 @@ __global__ __launch_bounds__(1024) void k_csr(const int32_t* __restrict__ rank, 
 // 16-byte residual rows written at their CSR position. W is read exactly once.
 // ---------------------------------------------------------------------------
 
+// 8 codes as two's-complement nibbles (code i in bits 4i..4i+3), the input of code_word
 __device__ __forceinline__ uint32_t pack8(const int* c) {
     uint32_t v = 0;
 #pragma unroll
@@ -485,8 +507,10 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64
             qc[i] = static_cast<int>(o.q);
             rc[i] = static_cast<int>(o.r);
         }
-        uint4 cq = make_uint4(pack8(qc), pack8(qc + 8), pack8(qc + 16), pack8(qc + 24));
-        uint4 cr = make_uint4(pack8(rc), pack8(rc + 8), pack8(rc + 16), pack8(rc + 24));
+        uint4 cq = make_uint4(code_word(pack8(qc)), code_word(pack8(qc + 8)), code_word(pack8(qc + 16)),
+                              code_word(pack8(qc + 24)));
+        uint4 cr = make_uint4(code_word(pack8(rc)), code_word(pack8(rc + 8)), code_word(pack8(rc + 16)),
+                              code_word(pack8(rc + 24)));
         // Rare: a quotient within 4e-6 of a rounding boundary. The wave repairs each
         // flagged lane L together: lane i < 32 requantizes weight i of L's 32 with
         // the exact quantizer, and L gathers the codes through LDS.
@@ -511,8 +535,8 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64
                     q4[i >> 3] |= static_cast<uint32_t>(fix[wave][i]) << (4 * (i & 7));
                     r4[i >> 3] |= static_cast<uint32_t>(fix[wave][32 + i]) << (4 * (i & 7));
                 }
-                cq = make_uint4(q4[0], q4[1], q4[2], q4[3]);
-                cr = make_uint4(r4[0], r4[1], r4[2], r4[3]);
+                cq = make_uint4(code_word(q4[0]), code_word(q4[1]), code_word(q4[2]), code_word(q4[3]));
+                cr = make_uint4(code_word(r4[0]), code_word(r4[1]), code_word(r4[2]), code_word(r4[3]));
             }
             __builtin_amdgcn_wave_barrier();
         }

@@ -16,22 +16,27 @@
  *     asynchronous on it unless stated otherwise.
  *   - Inputs are read-only. Outputs are fully overwritten. Inputs and outputs
  *     must not overlap.
- *   - int4 data are two's-complement nibbles; the low nibble of each byte holds
- *     the even input index.
+ *   - int4 codes (values in [-7, 7]) are packed eight to a little-endian 32-bit
+ *     word, inputs k0..k0+7 with k0 a multiple of 8: nibble e of the word (bits
+ *     4e..4e+3) holds |c_e| in its low three bits and, in its high bit, the sign
+ *     of code (e - 1) mod 8 (1 = negative; zero has no sign). With this encoding
+ *     word & 0x87878787 and rotr(word, 4) & 0x87878787 are the fp8 (e4m3) MFMA
+ *     operand bytes of the even and the odd codes (value c * 2^-9, exact).
  *   - Packed layouts (G = K/128 groups, G4 = ceil(G/4)). Each is chosen so that one
  *     64-lane 16-byte load of the GEMM reads 1 KB of contiguous memory:
- *       xq  activations, group-major: byte (g, m, j) at (g*M + m)*64 + j holds
- *           inputs k = 128g + 2j (low nibble) and 128g + 2j + 1 of token m.
+ *       xq  activations, group-major: the word at byte (g*M + m)*64 + 4i holds
+ *           inputs 128g + 8i .. 128g + 8i + 7 of token m.
  *       wq  base codes, tiled by 16 rows x 1 group: row n, group g, byte j (0..63)
- *           of the row's 64-byte group chunk is at
+ *           of the row's 64-byte group chunk (words in input order) is at
  *             ((n/16)*G + g)*1024 + ((j/16)*16 + n%16)*16 + j%16.
  *       sw  fp16 group scales, four groups per row entry: scale (n, g) is element
  *             (((n/16)*G4 + g/4)*16 + n%16)*4 + g%4   of a u16 array of N*G4*4;
  *           entries of groups g >= G are zero.
- *       rq  residual codes of the chosen blocks, [nnz][bn][bk/2], rows contiguous.
+ *       rq  residual codes of the chosen blocks, [nnz][bn][bk/2], rows contiguous
+ *           (8 words of 8 codes per block row).
  *     Sizes: xq M*K/2 bytes, wq N*K/2 bytes, sw N*G4*4 u16, rq nnz*bn*bk/2 bytes.
- *   - Packed buffers (xq, wq, rq) and the fp32 w and h must be 16-byte aligned;
- *     sw must be 8-byte aligned.
+ *   - Packed buffers (xq, wq, rq), the activations x and the fp32 w and h must be
+ *     16-byte aligned; sw must be 8-byte aligned.
  *   - Argument checks happen before any launch and return MQ_ERR_INVALID_ARG or
  *     MQ_ERR_UNSUPPORTED with nothing written. A failed launch returns
  *     MQ_ERR_HIP; faults inside a kernel surface at the caller's next
@@ -80,8 +85,8 @@ int mq_hessian_diag(const void* x, int x_dtype, int64_t M, int64_t K, float* h, 
  * pipeline, Methodology 3).
  *   sx[m] = fp32(max_k |x[m][k]| / 7)
  *   xq[m][k] = sx[m] == 0 ? 0 : clamp(rint(x[m][k] / sx[m]), -7, 7)   (ties to even)
- * x: [M][K] fp32 or bf16 (row-major), xq: M*K/2 bytes in the group-major layout
- * above, sx: fp32 [M]. K % 128 == 0.
+ * x: [M][K] fp32 or bf16 (row-major, 16-byte aligned), xq: M*K/2 bytes in the
+ * group-major layout above, sx: fp32 [M]. K % 128 == 0.
  */
 int mq_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* xq, float* sx,
                     void* stream);
@@ -130,8 +135,9 @@ int mq_pack_weights(const float* w, int64_t N, int64_t K, int group, int bn, int
 /*
  * The fused ZipperEngine GEMM (Methodology 3): one kernel streams the packed base
  * and, inside the same K-loop, the residual blocks listed for its rows; both
- * products accumulate into the same exact int32 partial sums per 128-group, which
- * are dequantized and summed in fp32:
+ * products are summed exactly per 128-group (integers; the fp8 MFMA returns them
+ * scaled by 2^-18 without rounding), and the group sums are dequantized and
+ * summed in fp32:
  *   T[m][n][g] = 14 * P + Pr,  P = sum_{k in g} xq*q,  Pr = sum over chosen blocks in g of xq*r
  *   y[m][n]    = sx[m] * sum_g ( groups with a chosen block in this row: s_r * T,
  *                                otherwise s * P )            (fp32; s_r = fp32(s/14))

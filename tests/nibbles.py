@@ -2,10 +2,14 @@
 
 Written independently of both the oracle's C code and the HIP library, so a
 mistake in either one's nibble order or sign handling shows up as a mismatch.
-Format: two's-complement int4, low nibble holds the even index. The oracle
-returns row-major arrays; the library's packed layouts (described in
-include/mq.h) are converted back to row-major here with reshapes and transposes
-only, so the comparison is element by element.
+The oracle packs two's-complement int4 codes, low nibble = even index, in
+row-major arrays. The library packs the same codes in its own word encoding
+(include/mq.h: per 32-bit word of 8 consecutive codes, nibble e holds |c_e| in
+its low three bits and the sign of code (e - 1) mod 8 in its high bit) and in
+tiled layouts. The converters below undo the layouts with reshapes and
+transposes only and the word encoding with a decoder written from that
+definition; the decoder also re-encodes and insists on the same bytes, so an
+invalid word (a negative zero, a stray bit) fails the comparison.
 """
 import numpy as np
 
@@ -21,6 +25,47 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
     out[..., 0::2] = lo
     out[..., 1::2] = hi
     return out
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """int [..., K] (values in [-8, 7]) -> two's-complement nibbles uint8 [..., K/2]"""
+    c = np.asarray(codes).astype(np.int64) & 15
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def lib_codes(packed: np.ndarray) -> np.ndarray:
+    """library word encoding, uint8 [..., 4W] -> int8 codes [..., 8W]"""
+    p = np.asarray(packed, dtype=np.uint8)
+    assert p.shape[-1] % 4 == 0
+    nib = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), np.uint8)
+    nib[..., 0::2] = p & 0x0F
+    nib[..., 1::2] = p >> 4
+    mag = (nib & 7).astype(np.int8)
+    top = (nib >> 3).reshape(nib.shape[:-1] + (-1, 8))
+    # the high bit of nibble e is the sign of code e - 1: code c's sign sits in nibble c + 1
+    sign = np.roll(top, -1, axis=-1).reshape(nib.shape)
+    codes = np.where(sign == 1, -mag, mag).astype(np.int8)
+    again = lib_pack(codes)
+    if not np.array_equal(again, p):
+        bad = np.argwhere(again != p)[0]
+        raise AssertionError(f"invalid library code word at byte {tuple(bad)}: {p[tuple(bad)]:#04x}")
+    return codes
+
+
+def lib_pack(codes: np.ndarray) -> np.ndarray:
+    """int codes [..., 8W] in [-7, 7] -> library word encoding uint8 [..., 4W]"""
+    c = np.asarray(codes).astype(np.int64)
+    assert c.shape[-1] % 8 == 0 and np.all(np.abs(c) <= 7)
+    mag = np.abs(c)
+    neg = (c < 0).astype(np.int64).reshape(c.shape[:-1] + (-1, 8))
+    top = np.roll(neg, 1, axis=-1).reshape(c.shape)     # nibble e carries the sign of code e - 1
+    nib = mag | (top << 3)
+    return (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+
+
+def lib_to_twos(packed: np.ndarray) -> np.ndarray:
+    """library word encoding -> the oracle's two's-complement nibble bytes (same shape)"""
+    return pack_int4(lib_codes(packed))
 
 
 def f16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -54,16 +99,22 @@ def rel_err(y, y_ref) -> float:
 
 # ---- the library's packed layouts -> row-major -----------------------------
 def xq_to_rowmajor(dev: np.ndarray, M: int, K: int) -> np.ndarray:
-    """group-major [K/128][M][64] bytes -> [M][K/2]"""
+    """group-major [K/128][M][64] library bytes -> [M][K/2] two's-complement nibbles"""
     a = np.asarray(dev, np.uint8).reshape(K // 128, M, 64)
-    return a.transpose(1, 0, 2).reshape(M, K // 2)
+    return lib_to_twos(a.transpose(1, 0, 2).reshape(M, K // 2))
 
 
 def wq_to_rowmajor(dev: np.ndarray, N: int, K: int) -> np.ndarray:
-    """tiles [N/16][G][kc 4][row 16][16 B] -> [N][K/2]"""
+    """tiles [N/16][G][kc 4][row 16][16 B] library bytes -> [N][K/2] two's-complement nibbles"""
     G = K // 128
     a = np.asarray(dev, np.uint8).reshape(N // 16, G, 4, 16, 16)
-    return a.transpose(0, 3, 1, 2, 4).reshape(N, K // 2)
+    return lib_to_twos(a.transpose(0, 3, 1, 2, 4).reshape(N, K // 2))
+
+
+def rq_to_twos(dev: np.ndarray) -> np.ndarray:
+    """residual payload [nnz][bn][32] library bytes -> two's-complement nibbles"""
+    a = np.asarray(dev, np.uint8)
+    return lib_to_twos(a) if a.size else a.copy()
 
 
 def sw_to_rowmajor(dev: np.ndarray, N: int, K: int):

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import synth
-from tests.nibbles import rel_err, sw_to_rowmajor, wq_to_rowmajor, xq_to_rowmajor
+from tests.nibbles import rel_err, rq_to_twos, sw_to_rowmajor, wq_to_rowmajor, xq_to_rowmajor
 
 pytestmark = pytest.mark.gpu
 
@@ -130,7 +130,7 @@ def _check(mq, orc, inp, k_blocks, out_dtype_name="bf16", rows=None, check_varia
     sw, pad = sw_to_rowmajor(_np(g["sw"]), cfg.N, cfg.K)
     np.testing.assert_array_equal(sw, ref["sw"])
     assert not pad.any(), "padding slots of sw must be zero"
-    np.testing.assert_array_equal(_np(g["rq"]), ref["rq"])
+    np.testing.assert_array_equal(rq_to_twos(_np(g["rq"])), ref["rq"])
     np.testing.assert_array_equal(xq_to_rowmajor(_np(g["xq"]), cfg.M, cfg.K), pre["xq"])
     np.testing.assert_array_equal(_np(g["sx"]), pre["sx"])
     sel = slice(None) if rows is None else rows
