@@ -71,7 +71,7 @@ struct DecStep {
     uint4 w[QS];         // base nibbles of the step's groups
     uint4 x[MT][QS];     // activation nibbles
     uint4 r[QS];         // residual nibbles (zero where no chosen block)
-    uint32_t s[QS / 2];  // the row's fp16 group scales, two per word
+    uint32_t s[(QS + 1) / 2];   // the row's fp16 group scales, two per word
     int rg;              // bit u: group g0+u holds a chosen block in this block row
 };
 
@@ -99,9 +99,11 @@ __device__ __forceinline__ void dec_fetch_main(DecStep<MT, QS>& st, const DecSrc
     if (QS == 4) {
         const uint2 v = buf_load8(src.s, so);
         st.s[0] = v.x;
-        st.s[QS / 2 - 1] = v.y;
-    } else {
+        st.s[(QS + 1) / 2 - 1] = v.y;
+    } else if (QS == 2) {
         st.s[0] = buf_load4(src.s, so);
+    } else {
+        st.s[0] = __builtin_amdgcn_raw_buffer_load_b16(src.s, so, 0, 0);
     }
 }
 
@@ -145,28 +147,34 @@ __device__ __forceinline__ void dec_compute(const DecStep<MT, QS>& st, const Gem
         if (g >= G) break;
         const float sc = f16_bits_to_f32(static_cast<uint16_t>(st.s[u >> 1] >> (16 * (u & 1))));
         const bool res = RES && ((st.rg >> u) & 1);
-        const v8i b = f8_operand(st.w[u]);
         if (res) {
-            const v8i rb = f8_operand(st.r[u]);
+            // the base products of both row tiles first, then the residual MFMAs
+            // accumulating onto 14 P (T = 14 P + Pr, exact): the base and the
+            // residual operands are never live together
             const float fr = (sc / 14.0f) * kF8Unit;
+            v4f tv[MT];
+            {
+                const v8i b = f8_operand(st.w[u]);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) tv[t] = mfma_f8(f8_operand(st.x[t][u]), b, v4f{0.0f, 0.0f, 0.0f, 0.0f}) * 14.0f;
+            }
+            const v8i rb = f8_operand(st.r[u]);
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
-                const v8i av = f8_operand(st.x[t][u]);
-                const v4f p = mfma_f8(av, b, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-                const v4f pr = mfma_f8(av, rb, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                tv[t] = mfma_f8(f8_operand(st.x[t][u]), rb, tv[t]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float tt = fmaf(14.0f, p[r], pr[r]);
-                    acc[t][r] = fmaf(fr, tt, acc[t][r]);
+                    acc[t][r] = fmaf(fr, tv[t][r], acc[t][r]);
                     if (DUMP) {
                         const int m = t * 16 + kg * 4 + r;
                         if (m < a.M)
-                            a.acc_dump[(static_cast<int64_t>(m) * a.N + n) * G + g] = static_cast<int>(tt * kF8Unit);
+                            a.acc_dump[(static_cast<int64_t>(m) * a.N + n) * G + g] = static_cast<int>(tv[t][r] * kF8Unit);
                     }
                 }
             }
         } else {
             const float f = sc * kF8Unit;
+            const v8i b = f8_operand(st.w[u]);
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 const v4f p = mfma_f8(f8_operand(st.x[t][u]), b, v4f{0.0f, 0.0f, 0.0f, 0.0f});
@@ -186,7 +194,9 @@ __device__ __forceinline__ void dec_compute(const DecStep<MT, QS>& st, const Gem
 
 template <int MT, bool RES, bool DUMP, int OUTMODE>
 __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a) {
-    constexpr int QS = 2;
+    // two groups per step; one for the residual variant with two row tiles,
+    // which keeps its registers within four waves per SIMD
+    constexpr int QS = (RES && MT == 2) ? 1 : 2;
     __shared__ float red[kMaxDecodeWaves * MT * 256];
     __shared__ int tab[RES ? 8 * (kMaxGroups / 4) : 1];   // column block -> CSR position
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
