@@ -1,25 +1,35 @@
-"""Benchmark of the MosaicQuant path on one MI355X.
+"""Benchmark of the MosaicQuant ZipperEngine path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--budget PCT]
+    python bench.py --sweep           # batch sweep and a LLaMA3-8B-shaped linear stack
 
-A step is one pass of the whole path over one batch of synthetic input, every
-step on the GPU: the diagonal-Hessian estimate of the batch, Delta-score top-K
-block selection, packing of the 4-bit base and residual, per-token activation
-quantization and the fused W4A4 + sparse-residual GEMM. Inputs are resident in
-HBM before the timed region; consecutive steps read different copies of them
-(more than 600 MB in total) so the 256 MB Infinity Cache cannot serve them.
+A step is one pass of the per-call path over one batch of synthetic input, on
+the GPU: per-token int4 activation quantization (mq_quantize_act), then the fused
+W4A4 + sparse-residual GEMM (mq_gemm_w4a4_residual). The layer's weights are
+prepared once beforehand (Hessian diagonal, Delta-score top-K, packing: the
+offline steps) and copied so that consecutive steps read different weight and
+activation copies (more than 600 MB in total): neither the 256 MB Infinity
+Cache nor L2 can serve them. Inputs are resident in HBM before the timed region.
 
-Printed on stdout: one JSON line. `value` is the step's algorithmic HBM bytes
-per second, the step timed as one replay of a HIP graph of `steps` steps;
-`roofline` is the call that takes most of the step, timed alone in its own graph
-with HIP events on the launch stream; `gemm` is the fused kernel alone (the metric's
-TOPS and GB/s), timed over rotated packed-weight copies, beside the dense-only
-kernel and the separate-kernel alternative; `cpu_baseline` is the CPU oracle on
-the host, one core, on the same workload.
+Printed on stdout: one JSON line.
+  value      algorithmic ops of the step (2*M*(N*K + nnz*bn*bk)) / step time, in TOPS;
+             the K steps are one replay of a HIP graph, HIP events around it
+  roofline   the fused GEMM kernel alone (the step's dominant kernel): its
+             algorithmic ops (MFMA-bound, M > 32) or bytes (HBM-bound, M <= 32)
+             per launch over its average launch duration (back-to-back launches
+             in a HIP graph, HIP events on the launch stream), against the
+             published MI355X peak
+  gemm       the fused kernel beside the dense-only kernel and the separate-kernel
+             alternative on the same workload (fusion overhead)
+  legs       the same three variants, plus a bf16 torch.matmul of the same layer,
+             on every other workload (decode shapes, budget sweeps)
+  cpu_baseline  the CPU oracle's per-call path (quantize, exact group sums,
+             output) on a bounded sample of the workload's tokens
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,8 +44,16 @@ import synth  # noqa: E402
 
 METRIC = "fused W4A4+10% residual GEMM: TOPS & HBM GB/s (% roofline); overhead vs dense"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
-INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 MFMA
+F8_PEAK_TOPS = 5000.0           # MI355X dense fp8 (and int8) MFMA
 ROTATE_BYTES = 640 << 20        # > 2 x (256 MB Infinity Cache + 8 x 4 MB L2)
+GEMM_SRC = os.path.join("dense_sparse_bit_amd", "csrc", "gemm.hip")
+TRAFFIC_SUMMARY = os.path.join("profiles", "gemm_fused_qwen3_14b_prefill_hbm_traffic.txt")
+
+# workloads measured beside the headline in one default run: (config, budgets in %)
+LEGS = [("llama3_8b_qo", (10,)),
+        ("llama3_8b_up_m4", (0, 5, 10, 20)), ("llama3_8b_up_m32", (0, 5, 10, 20)),
+        ("llama3_8b_down_m4", (0, 5, 10, 20)), ("llama3_8b_down_m32", (0, 5, 10, 20)),
+        ("qwen3_32b_up", (10,)), ("qwen3_32b_down", (10,))]
 
 
 def log(*a):
@@ -44,6 +62,8 @@ def log(*a):
 
 # --------------------------------------------------------------------------- algorithmic work
 def gemm_bytes(cfg, nnz, residual=True, y_bytes=2):
+    """Bytes the GEMM must move at minimum: base nibbles, fp16 group scales, activation
+    nibbles and scales, the output; plus residual nibbles and the CSR lists."""
     M, N, K, G = cfg.M, cfg.N, cfg.K, cfg.K // cfg.group
     b = N * K // 2 + N * G * 2 + M * K // 2 + M * 4 + M * N * y_bytes
     if residual:
@@ -55,21 +75,11 @@ def gemm_ops(cfg, nnz, residual=True):
     return 2 * cfg.M * (cfg.N * cfg.K + (nnz * cfg.bn * cfg.bk if residual else 0))
 
 
-def step_bytes(cfg, nnz, x_bytes):
-    """Bytes each call of the step must move at minimum (read inputs once, write outputs once)."""
-    M, N, K, G = cfg.M, cfg.N, cfg.K, cfg.K // cfg.group
-    nb = (N // cfg.bn) * (K // cfg.bk)
-    csr = (N // cfg.bn + 1) * 4 + nnz * 4
-    return {
-        "hessian_diag": M * K * x_bytes + K * 4,
-        "select_blocks": N * K * 4 + K * 4 + nb * 8 + csr,
-        "pack_weights": N * K * 4 + csr + N * K // 2 + N * G * 2 + nnz * cfg.bn * cfg.bk // 2,
-        "quantize_act": M * K * x_bytes + M * K // 2 + M * 4,
-        "gemm_w4a4_residual": gemm_bytes(cfg, nnz),
-    }
+def roofline_kind(cfg):
+    return "mfma" if cfg.M > 32 else "hbm"
 
 
-# --------------------------------------------------------------------------- GPU legs
+# --------------------------------------------------------------------------- GPU helpers
 def _graph_time_us(torch, fn, n_calls, reps=5):
     """Median per-call time of `n_calls` back-to-back calls of fn(i) captured in one
     HIP graph (HIP events around each replay, on the capturing stream)."""
@@ -95,76 +105,166 @@ def _graph_time_us(torch, fn, n_calls, reps=5):
     return float(np.median(times[1:]))
 
 
-def bench_step(mq, torch, cfg, inp, k_blocks, steps, warmup):
-    """The whole path, step after step, over rotating input copies. The timed
-    region is one replay of a HIP graph holding exactly `steps` steps (launch
-    overhead of the Python binding excluded); each call is also timed alone."""
-    dev = torch.device("cuda:0")
-    x_bytes = 2 if inp.X_bits is not None else 4
-    per_copy = cfg.N * cfg.K * 4 + cfg.M * cfg.K * x_bytes
-    copies = max(2, min(64, -(-ROTATE_BYTES // per_copy)))
+def _x_device(torch, inp, dev):
     if inp.X_bits is not None:
-        x0 = torch.from_numpy(inp.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    else:
-        x0 = torch.from_numpy(inp.X).to(dev)
-    w0 = torch.from_numpy(inp.W).to(dev)
-    xs = [x0.clone() for _ in range(copies)]
-    ws = [w0.clone() for _ in range(copies)]
-    del x0, w0
-    N, K, M, bn = cfg.N, cfg.K, cfg.M, cfg.bn
-    G = K // 128
-    nb = (N // bn) * (K // cfg.bk)
-    h = torch.empty(K, dtype=torch.float32, device=dev)
-    sel_out = (torch.empty(N // bn + 1, dtype=torch.int32, device=dev),
-               torch.empty(max(k_blocks, 1), dtype=torch.int32, device=dev),
-               torch.empty(nb, dtype=torch.float64, device=dev))
-    sel_ws = mq.select_workspace(N, K, bn=bn, device=dev)
-    pack_out = (torch.empty((N // 16, G, 1024), dtype=torch.uint8, device=dev),
-                torch.empty((N // 16, (G + 3) // 4, 16, 4), dtype=torch.int16, device=dev),
-                torch.empty((max(k_blocks, 1), bn, 32), dtype=torch.uint8, device=dev))
-    xq = torch.empty((G, M, 64), dtype=torch.uint8, device=dev)
-    sx = torch.empty(M, dtype=torch.float32, device=dev)
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    gemm_ws = mq.workspace(M, N, K, device=dev)
-    log(f"[bench] step workload {cfg.name}: M={M} K={K} N={N} bn={bn} k_blocks={k_blocks}, "
-        f"{copies} input copies ({copies * per_copy / 2**20:.0f} MiB)")
+        return torch.from_numpy(inp.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(inp.X).to(dev)
 
-    def hess(i):
-        mq.hessian_diag(xs[i % copies], out=h)
 
-    def select(i):
-        return mq.select_blocks(ws[i % copies], h, k_blocks, bn=bn, out=sel_out, workspace=sel_ws)
+class Layer:
+    """One synthetic layer on the device: W, X, and the packed operands for a budget."""
 
-    def pack(i):
-        rp, ci = sel_out[0], sel_out[1][:k_blocks]
-        return mq.pack_weights(ws[i % copies], rp, ci, bn=bn, out=pack_out)
+    def __init__(self, mq, torch, cfg, inp=None):
+        self.mq, self.torch, self.cfg = mq, torch, cfg
+        self.inp = synth.make_inputs(cfg) if inp is None else inp
+        dev = torch.device("cuda:0")
+        self.x = _x_device(torch, self.inp, dev)
+        self.w = torch.from_numpy(self.inp.W).to(dev)
+        self.h = mq.hessian_diag(self.x)
+        self.xq, self.sx = mq.quantize_act(self.x)
 
-    def quant(i):
-        mq.quantize_act(xs[i % copies], xq=xq, sx=sx)
+    def pack(self, k_blocks):
+        mq, cfg = self.mq, self.cfg
+        rp, ci, _ = mq.select_blocks(self.w, self.h, k_blocks, bn=cfg.bn, return_delta=False)
+        wq, sw, rq = mq.pack_weights(self.w, rp, ci, bn=cfg.bn)
+        return dict(wq=wq, sw=sw, rq=rq, row_ptr=rp, col_idx=ci)
+
+    def copies(self, packed, nbytes):
+        n = max(2, min(256, -(-ROTATE_BYTES // max(nbytes, 1))))
+        return [{k: v.clone() for k, v in packed.items()} for _ in range(n)]
+
+
+def bench_variants(mq, torch, layer, k_blocks, calls, bf16=True):
+    """Fused, dense-only and separate-kernel GEMM (and a bf16 torch.matmul of the same
+    layer) over rotated weight copies, each in its own HIP graph of `calls`
+    back-to-back calls; every graph's output is checked against its eager call."""
+    cfg = layer.cfg
+    packed = layer.pack(k_blocks)
+    pbytes = gemm_bytes(cfg, k_blocks) - cfg.M * (cfg.K // 2 + 4 + cfg.N * 2)
+    sets = layer.copies(packed, pbytes)
+    n = len(sets)
+    xq, sx, K, bn = layer.xq, layer.sx, cfg.K, cfg.bn
+    y = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device="cuda")
+    wsb = torch.empty((cfg.M, cfg.N), dtype=torch.float32, device="cuda")
+
+    def fused(i):
+        s = sets[i % n]
+        mq.gemm_w4a4_residual(xq, sx, s["wq"], s["sw"], s["row_ptr"], s["col_idx"], s["rq"], K, bn=bn, y=y)
+
+    def dense(i):
+        s = sets[i % n]
+        mq.gemm_w4a4_dense(xq, sx, s["wq"], s["sw"], K, y=y)
+
+    def separate(i):
+        s = sets[i % n]
+        mq.gemm_residual_separate(xq, sx, s["wq"], s["sw"], s["row_ptr"], s["col_idx"], s["rq"], K,
+                                  bn=bn, y=y, ws=wsb)
+
+    out = {}
+    for name, fn in (("dense", dense), ("fused", fused), ("separate", separate)):
+        fn(calls - 1)
+        torch.cuda.synchronize()
+        y_eager = y.clone()
+        out[name] = _graph_time_us(torch, fn, calls)
+        if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
+            raise RuntimeError(f"graph replay of the {name} GEMM differs from the eager call")
+    del sets
+    if bf16:
+        # the W16A16 context: the same layer as a bf16 matmul (hipBLASLt), weights rotated too
+        wb = layer.w.to(torch.bfloat16)
+        xb = layer.x.to(torch.bfloat16)
+        nw = max(2, min(64, -(-ROTATE_BYTES // (wb.numel() * 2))))
+        ws_ = [wb.clone() for _ in range(nw)]
+        yb = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device="cuda")
+
+        def mm(i):
+            torch.matmul(xb, ws_[i % nw].t(), out=yb)
+        out["bf16_matmul"] = _graph_time_us(torch, mm, max(20, calls // 4))
+        del ws_, wb
+    torch.cuda.empty_cache()
+    return out
+
+
+def leg_record(cfg, pct, k_blocks, t):
+    fb, db = gemm_bytes(cfg, k_blocks), gemm_bytes(cfg, k_blocks, residual=False)
+    fo, do = gemm_ops(cfg, k_blocks), gemm_ops(cfg, k_blocks, residual=False)
+
+    def one(us, b, o):
+        return {"us": round(us, 3), "GB/s": round(b / us / 1e3, 1),
+                "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+                "TOPS": round(o / us / 1e6, 2), "mfma_frac": round(o / us / 1e6 / F8_PEAK_TOPS, 4)}
+    rec = {"workload": cfg.name, "M": cfg.M, "K": cfg.K, "N": cfg.N, "bn": cfg.bn, "budget_pct": pct,
+           "k_blocks": k_blocks, "bound": roofline_kind(cfg), "bytes": fb, "ops": fo,
+           "fused": one(t["fused"], fb, fo), "dense": one(t["dense"], db, do),
+           "separate": one(t["separate"], fb, fo),
+           "overhead_vs_dense": round(t["fused"] / t["dense"] - 1, 4),
+           "separate_overhead_vs_dense": round(t["separate"] / t["dense"] - 1, 4)}
+    if "bf16_matmul" in t:
+        rec["bf16_matmul_us"] = round(t["bf16_matmul"], 3)
+        rec["speedup_fused_vs_bf16"] = round(t["bf16_matmul"] / t["fused"], 3)
+    if "read_ceiling_us" in t:
+        rec["read_ceiling_us"] = round(t["read_ceiling_us"], 3)
+        rec["fused_vs_read_ceiling"] = round(t["read_ceiling_us"] / t["fused"], 4)
+    return rec
+
+
+def read_ceiling_us(torch, nbytes, calls=100):
+    """Time of a plain streaming read of `nbytes` (torch's sum over a float32 view),
+    over rotating slices of a 1 GiB buffer: the achievable read rate at this size."""
+    n = max(64, int(nbytes) // 4)
+    src = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    slices = max(1, src.numel() // n)
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def rd(i):
+        j = i % slices
+        torch.sum(src[j * n:(j + 1) * n], dim=0, out=out)
+    us = _graph_time_us(torch, rd, calls)
+    del src
+    torch.cuda.empty_cache()
+    return us
+
+
+# --------------------------------------------------------------------------- the headline step
+def bench_step(mq, torch, layer, k_blocks, steps, warmup):
+    """The per-call path (quantize activations, fused GEMM), step after step over
+    rotated weight and activation copies; K steps captured in one HIP graph and
+    timed as one replay. The fused GEMM is also timed alone (its launches back to
+    back in a graph, same copies): the roofline kernel's average launch time."""
+    cfg = layer.cfg
+    packed = layer.pack(k_blocks)
+    pbytes = gemm_bytes(cfg, k_blocks) - cfg.M * (cfg.K // 2 + 4 + cfg.N * 2)
+    sets = layer.copies(packed, pbytes)
+    n = len(sets)
+    nx = max(2, min(16, -(-(64 << 20) // (layer.x.numel() * layer.x.element_size()))))
+    xs = [layer.x.clone() for _ in range(nx)]
+    xq = torch.empty_like(layer.xq)
+    sx = torch.empty_like(layer.sx)
+    y = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device="cuda")
+    K, bn = cfg.K, cfg.bn
+    log(f"[bench] step workload {cfg.name}: M={cfg.M} K={K} N={cfg.N} bn={bn} k_blocks={k_blocks}, "
+        f"{n} weight copies ({n * pbytes / 2**20:.0f} MiB), {nx} activation copies")
 
     def gemm(i):
-        wq, sw, rq = pack_out[0], pack_out[1], pack_out[2][:k_blocks]
-        mq.gemm_w4a4_residual(xq, sx, wq, sw, sel_out[0], sel_out[1][:k_blocks], rq, K, bn=bn, y=y,
-                              workspace=gemm_ws)
+        s = sets[i % n]
+        mq.gemm_w4a4_residual(xq, sx, s["wq"], s["sw"], s["row_ptr"], s["col_idx"], s["rq"], K, bn=bn, y=y)
+
+    def quant(i):
+        mq.quantize_act(xs[i % nx], xq=xq, sx=sx)
 
     def one_step(i):
-        hess(i)
-        select(i)
-        pack(i)
         quant(i)
         gemm(i)
 
     for i in range(warmup):
         one_step(i)
     torch.cuda.synchronize()
-    # eager steps (Python launch path included), for reference
     t0 = time.perf_counter()
     for i in range(steps):
         one_step(i)
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
 
-    # the timed region: one replay of a graph of exactly `steps` steps
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -185,142 +285,71 @@ def bench_step(mq, torch, cfg, inp, k_blocks, steps, warmup):
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     gpu_ms = e0.elapsed_time(e1) / steps
     del graph
-
-    # each call alone, back to back over the copies, in its own graph
-    calls = 2 * copies
-    us = {"hessian_diag": _graph_time_us(torch, hess, calls),
-          "select_blocks": _graph_time_us(torch, select, calls),
-          "pack_weights": _graph_time_us(torch, pack, calls),
-          "quantize_act": _graph_time_us(torch, quant, calls),
-          "gemm_w4a4_residual": _graph_time_us(torch, gemm, calls)}
-    for n, v in us.items():
-        log(f"[bench] {n}: {v:.3f} us per call")
-    log(f"[bench] step: {gpu_ms * 1e3:.2f} us (graph), {eager_ms * 1e3:.2f} us (eager Python launches)")
-    return dict(gpu_ms=gpu_ms, wall_ms=wall_ms, eager_ms=eager_ms, us=us, copies=copies)
-
-
-def bench_gemm(mq, torch, cfg, inp, k_blocks, calls):
-    """Fused, dense-only and separate-kernel GEMM over rotated packed-weight copies,
-    each in its own HIP graph of `calls` back-to-back calls; every variant's graph
-    output is checked against its eager call."""
-    dev = torch.device("cuda:0")
-    if inp.X_bits is not None:
-        x = torch.from_numpy(inp.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    else:
-        x = torch.from_numpy(inp.X).to(dev)
-    w = torch.from_numpy(inp.W).to(dev)
-    g = mq.forward_layer(x, w, k_blocks, bn=cfg.bn)
-    del w
-    packed = gemm_bytes(cfg, k_blocks) - cfg.M * (cfg.K // 2 + 4 + cfg.N * 2)
-    copies = max(2, min(256, -(-ROTATE_BYTES // packed)))
-    sets = [(g["wq"].clone(), g["sw"].clone(), g["rq"].clone(), g["row_ptr"].clone(),
-             g["col_idx"].clone()) for _ in range(copies)]
-    xq, sx, K, bn = g["xq"], g["sx"], cfg.K, cfg.bn
-    y = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device=dev)
-    wsb = torch.empty((cfg.M, cfg.N), dtype=torch.float32, device=dev)
-    gws = mq.workspace(cfg.M, cfg.N, K, device=dev)
-    log(f"[bench] gemm legs: {copies} packed-weight copies ({copies * packed / 2**20:.0f} MiB), "
-        f"{calls} calls each")
-
-    def fused(i):
-        wq, sw, rq, rp, ci = sets[i % copies]
-        mq.gemm_w4a4_residual(xq, sx, wq, sw, rp, ci, rq, K, bn=bn, y=y, workspace=gws)
-
-    def dense(i):
-        wq, sw, *_ = sets[i % copies]
-        mq.gemm_w4a4_dense(xq, sx, wq, sw, K, y=y, workspace=gws)
-
-    def separate(i):
-        wq, sw, rq, rp, ci = sets[i % copies]
-        mq.gemm_residual_separate(xq, sx, wq, sw, rp, ci, rq, K, bn=bn, y=y, ws=wsb, workspace=gws)
-
-    out = {}
-    for name, fn in (("dense", dense), ("fused", fused), ("separate", separate)):
-        # eager result of the last call, to check the graph replays against
-        fn(calls - 1)
-        torch.cuda.synchronize()
-        y_eager = y.clone()
-        out[name] = _graph_time_us(torch, fn, calls)
-        if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
-            raise RuntimeError(f"graph replay of the {name} GEMM differs from the eager call")
-        log(f"[bench] gemm {name}: {out[name]:.3f} us/call")
-    return out
-
-
-# --------------------------------------------------------------------------- calibration
-def calibrate(torch, sizes_mb=(9.65, 64.0, 512.0), calls=50):
-    """Achievable HBM rate of a plain device copy (torch's copy kernel) at the sizes
-    this path moves, over rotating slices of a 1 GiB source so the Infinity Cache
-    cannot serve the reads; and the duration of a one-element fill (launch floor)."""
-    dev = torch.device("cuda:0")
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    src.fill_(1)
-    out = {}
-    for mb in sizes_mb:
-        n = int(mb * 1e6) // 256 * 256
-        dst = torch.empty(n, dtype=torch.uint8, device=dev)
-        slices = max(1, (1 << 30) // n)
-        for i in range(5):
-            dst.copy_(src[(i % slices) * n:(i % slices) * n + n])
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(calls):
-            j = i % slices
-            dst.copy_(src[j * n:j * n + n])
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / calls
-        out[f"copy_{mb:g}MB"] = {"us": round(us, 3), "GB/s(read+write)": round(2 * n / us / 1e3, 1)}
-        log(f"[bench] calib copy {mb:g} MB: {us:.2f} us/call, {2 * n / us / 1e3:.0f} GB/s read+write")
-        del dst
-    tiny = torch.empty(1, dtype=torch.float32, device=dev)
+    # the last step's output against its eager call (same inputs, same kernels)
+    y_graph = y.clone()
+    one_step(steps - 1)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(200):
-        tiny.fill_(1.0)
-    e1.record()
-    torch.cuda.synchronize()
-    out["fill_1_element_us"] = round(e0.elapsed_time(e1) * 1e3 / 200, 3)
-    del src
+    if not torch.equal(y.view(torch.int16), y_graph.view(torch.int16)):
+        raise RuntimeError("graph replay of the step differs from the eager step")
+
+    gemm_us = _graph_time_us(torch, gemm, max(steps, 2 * n))
+    quant_us = _graph_time_us(torch, quant, max(steps, 2 * nx))
+    log(f"[bench] step {gpu_ms * 1e3:.2f} us (graph), eager {eager_ms * 1e3:.2f} us; "
+        f"fused GEMM alone {gemm_us:.3f} us, quantize_act alone {quant_us:.3f} us")
+    del sets, xs
     torch.cuda.empty_cache()
-    return out
+    return dict(gpu_ms=gpu_ms, wall_ms=wall_ms, eager_ms=eager_ms, gemm_us=gemm_us, quant_us=quant_us,
+                copies=n)
 
 
 # --------------------------------------------------------------------------- CPU oracle leg
-def cpu_baseline(cfg, inp, k_blocks, seconds, step_total_bytes):
+def cpu_baseline(cfg, inp, k_blocks, rows):
+    """The oracle's per-call path (O1 activation quantization, O8 exact group sums,
+    O9 output) on the first `rows` tokens and every output; its weight preparation
+    (selection, packing) is done beforehand and not timed."""
     import oracle
     orc = oracle.Oracle()
-    runs, t0 = 0, time.perf_counter()
-    while True:
-        orc.forward(inp.x_raw(), inp.W, k_blocks, cfg.group, cfg.bn, cfg.bk)
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or runs >= 50:
-            break
-    per = el / runs
-    return {"value": step_total_bytes / per / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{runs} full passes of the whole path on this workload (all steps, all "
-                      f"{cfg.M} tokens), single-threaded C, {per * 1e3:.0f} ms per pass",
-            "s_per_step": per}
+    xr = inp.x_raw()[:rows]
+    h = orc.hessian_diag(inp.x_raw())
+    rp, ci, _, _ = orc.select_blocks(inp.W, h, k_blocks, cfg.group, cfg.bn, cfg.bk)
+    wq, sw, rq = orc.pack_weights(inp.W, rp, ci, cfg.group, cfg.bn, cfg.bk)
+    t0 = time.perf_counter()
+    xq, sx = orc.quantize_act(xr)
+    P, Pr = orc.accumulators(xq, wq, rp, ci, rq, cfg.K, cfg.group, cfg.bn, cfg.bk)
+    orc.output(sx, sw, P, Pr)
+    el = time.perf_counter() - t0
+    ops = 2 * rows * (cfg.N * cfg.K + k_blocks * cfg.bn * cfg.bk)
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"value": round(ops / el / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"tokens 0-{rows - 1} of {cfg.M} x all {cfg.N} outputs x K={cfg.K} "
+                      f"(O1 quantize + O8 exact group sums + O9 fp64 output, single-threaded C), "
+                      f"{el:.1f} s", "seconds": round(el, 2),
+            "host_cores_available": avail, "host_nproc": os.cpu_count()}
 
 
 # --------------------------------------------------------------------------- profiles
 CALIB_COPY_BYTES = 256 << 20     # the copy of known size the HBM counters are scaled by
 
 
-def pmc_pass(mq, torch, cfg, inp, k_blocks):
-    """What `rocprofv3 --pmc` runs: a few whole steps, then CALIB_COPY_BYTES copied
-    device to device five times (a plain copy of known size, to scale the counters)."""
-    bench_step(mq, torch, cfg, inp, k_blocks, steps=3, warmup=1)
-    src = torch.ones(CALIB_COPY_BYTES, dtype=torch.uint8, device="cuda")
+def pmc_pass(mq, torch, cfg, k_blocks, calls=5):
+    """What `rocprofv3 --pmc` runs: a few fused GEMM calls and a few dense-only calls
+    of the workload, then CALIB_COPY_BYTES read and written by an elementwise kernel
+    (a copy of known size, to scale the counters)."""
+    layer = Layer(mq, torch, cfg)
+    p = layer.pack(k_blocks)
+    y = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device="cuda")
+    for _ in range(calls):
+        mq.gemm_w4a4_residual(layer.xq, layer.sx, p["wq"], p["sw"], p["row_ptr"], p["col_idx"], p["rq"],
+                              cfg.K, bn=cfg.bn, y=y)
+    for _ in range(calls):
+        mq.gemm_w4a4_dense(layer.xq, layer.sx, p["wq"], p["sw"], cfg.K, y=y)
+    src = torch.ones(CALIB_COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(5):
-        dst.copy_(src)                       # the runtime's blit copy
-    fsrc, fdst = src.view(torch.float32), dst.view(torch.float32)
-    for _ in range(5):
-        torch.mul(fsrc, 1.0, out=fdst)       # an elementwise kernel with 16-byte lane accesses
+        torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
 
 
@@ -333,11 +362,16 @@ def _db(path):
     return sqlite3.connect(dbs[0])
 
 
+def _src_digest():
+    return hashlib.sha256(open(os.path.join(ROOT, GEMM_SRC), "rb").read()).hexdigest()[:16]
+
+
 def profile_summary(db_path, title, command):
     """Kernel-trace statistics of a rocprofv3 results database, as text."""
     con = _db(db_path)
     rows = list(con.execute("select name, total_calls, total_duration, average, percentage from top_kernels"))
     out = [f"# {title}", "", f"command: {command}", "",
+           f"kernel source ({GEMM_SRC}) sha256: {_src_digest()}", "",
            "rocprofv3 --kernel-trace --stats, kernel durations (us):", "",
            f"{'calls':>6} {'avg_us':>10} {'total_us':>11} {'pct':>6}  kernel"]
     for name, calls, tot, avg, pct in rows:
@@ -346,72 +380,130 @@ def profile_summary(db_path, title, command):
 
 
 def _counter_means(db_path, counter):
-    """Mean of one counter per kernel name, and per-dispatch values of the two copy
-    kernels (runtime blit, elementwise multiply by one)."""
     con = _db(db_path)
-    per, blit, elem = {}, [], []
+    per, calib = {}, []
     for k, c, v, grid in con.execute(
             "select kernel_name, counter_name, value, grid_size from counters_collection"):
         if c != counter:
             continue
         per.setdefault(k, []).append(v)
-        if "copyBuffer" in k:
-            blit.append((grid, v))
         if "elementwise" in k and "Mul" in k:
-            elem.append((grid, v))
-    return {k: sum(v) / len(v) for k, v in per.items()}, blit, elem
+            calib.append((grid, v))
+    return {k: sum(v) / len(v) for k, v in per.items()}, calib
 
 
-def pmc_summary(fetch_db, write_db, title, commands):
-    """HBM traffic per dispatch from FETCH_SIZE and WRITE_SIZE passes, each scaled by
-    what the same counter reads for the largest copy (CALIB_COPY_BYTES each way)."""
-    fetch, fblit, felem = _counter_means(fetch_db, "FETCH_SIZE")
-    write, wblit, welem = _counter_means(write_db, "WRITE_SIZE")
+def counters_summary(db_paths, title, commands):
+    """Mean per dispatch of every counter in the given rocprofv3 --pmc databases, for
+    the library's kernels; FETCH_SIZE and WRITE_SIZE are also scaled to bytes by what
+    they read for the calibration copy (CALIB_COPY_BYTES read and written)."""
     kib = CALIB_COPY_BYTES / 1024
-
-    def largest(pairs):
-        big = max(g for g, _ in pairs)
-        return float(np.mean([v for g, v in pairs if g == big]))
-    bf, bw = largest(fblit), largest(wblit)
-    cf, cw = largest(felem), largest(welem)
-    ff, fw = kib / cf, kib / cw
-    import hashlib
-    digest = hashlib.sha256(open(os.path.join(ROOT, "dense_sparse_bit_amd", "csrc", "prep.hip"), "rb")
-                            .read()).hexdigest()[:16]
+    table, scale = {}, {}
+    for path in db_paths:
+        con = _db(path)
+        names = sorted({c for (c,) in con.execute("select distinct counter_name from counters_collection")})
+        for c in names:
+            per, calib = _counter_means(path, c)
+            for k, v in per.items():
+                if "mq::" in k:
+                    table.setdefault(k, {})[c] = v
+            if c in ("FETCH_SIZE", "WRITE_SIZE") and calib:
+                big = max(g for g, _ in calib)
+                scale[c] = kib / float(np.mean([v for g, v in calib if g == big]))
     out = [f"# {title}", "", "commands:"] + [f"  {c}" for c in commands] + [
-        "", f"kernel source (dense_sparse_bit_amd/csrc/prep.hip) source sha256: {digest}"] + [
-        "", f"calibration: {CALIB_COPY_BYTES >> 20} MiB read and written by an elementwise kernel "
-        f"(y = x * 1, 16-byte lane accesses like this library's): FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE "
-        f"{cw:.0f} KiB per dispatch -> scale factors {ff:.4f} (fetch), {fw:.4f} (write), used below",
-        f"(the runtime blit copy of the same size reads FETCH_SIZE {bf:.0f} KiB, WRITE_SIZE {bw:.0f} KiB: "
-        f"factors {kib / bf:.4f}, {kib / bw:.4f}; its request sizes differ)", "",
-        f"{'fetch_KiB':>12} {'write_KiB':>12} {'scaled_MB':>10}  kernel"]
-    for k in sorted(set(fetch) | set(write), key=lambda n: -fetch.get(n, 0)):
-        if "mq::" not in k:
-            continue
-        f, w = fetch.get(k, 0.0), write.get(k, 0.0)
-        out.append(f"{f:>12.1f} {w:>12.1f} {(f * ff + w * fw) * 1024 / 1e6:>10.3f}  {k[:100]}")
+        "", f"kernel source ({GEMM_SRC}) sha256: {_src_digest()}", ""]
+    if scale:
+        out.append("calibration: an elementwise kernel reading and writing "
+                   f"{CALIB_COPY_BYTES >> 20} MiB; bytes per KiB of counter: " +
+                   ", ".join(f"{c} x{v * 1024:.1f}" for c, v in sorted(scale.items())))
+        out.append("")
+    for k in sorted(table):
+        out.append(f"kernel {k[:120]}")
+        for c, v in sorted(table[k].items()):
+            extra = ""
+            if c in scale:
+                extra = f"   -> {v * scale[c] * 1024 / 1e6:.3f} MB per dispatch"
+            out.append(f"  {c:<28} {v:>16.1f}{extra}")
+        out.append("")
     return "\n".join(out)
 
 
-def traffic_from_profile(kernels, source):
-    """HBM bytes per call of the given kernels from the committed counter summary,
-    or None when the summary is missing or was taken from different kernel source."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", "select_blocks_llama3_8b_qo_hbm_traffic.txt")
+def traffic_from_profile(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when
+    the summary is missing or was taken from different kernel source."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    digest = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()[:16]
-    if f"source sha256: {digest}" not in text:
+    if f"sha256: {_src_digest()}" not in text:
         return None
-    total = 0.0
-    for k in kernels:
-        line = [l for l in text.splitlines() if l.rstrip().endswith(k) or f" {k}(" in l]
-        if not line:
-            return None
-        total += float(line[0].split()[2]) * 1e6
-    return total
+    lines = text.splitlines()
+    total, found = 0.0, 0
+    for i, l in enumerate(lines):
+        if l.startswith("kernel ") and kernel in l:
+            for l2 in lines[i + 1:]:
+                if l2.startswith("kernel "):
+                    break
+                if ("FETCH_SIZE" in l2 or "WRITE_SIZE" in l2) and "MB per dispatch" in l2:
+                    total += float(l2.split("->")[1].split()[0]) * 1e6
+                    found += 1
+            break
+    return int(total) if found == 2 else None
+
+
+# --------------------------------------------------------------------------- sweep (batch sizes, layer stack)
+def sweep(mq, torch, calls):
+    """Fused, dense-only, separate and bf16 matmul at M = 1..256 on the LLaMA3-8B-shaped
+    MLP up layer (10%), and a LLaMA3-8B-shaped linear stack (q, k, v, o, gate, up,
+    down; per-layer activation quantization + fused GEMM vs bf16 matmuls) end to end."""
+    res = {"batch": [], "stack": []}
+    for M in (1, 2, 4, 8, 16, 24, 32, 64, 128, 256):
+        cfg = synth.custom_config(f"llama3_8b_up_m{M}", M=M, K=4096, N=14336, bn=64)
+        layer = Layer(mq, torch, cfg)
+        kb = cfg.k_blocks(10)
+        t = bench_variants(mq, torch, layer, kb, calls)
+        rec = leg_record(cfg, 10, kb, t)
+        res["batch"].append(rec)
+        log(f"[sweep] M={M}: fused {t['fused']:.2f} dense {t['dense']:.2f} sep {t['separate']:.2f} "
+            f"bf16 {t['bf16_matmul']:.2f} us")
+        del layer
+    shapes = [("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024), ("o", 4096, 4096),
+              ("gate", 4096, 14336), ("up", 4096, 14336), ("down", 14336, 4096)]
+    for M in (1, 4, 16, 32):
+        layers = []
+        for nm, K, N in shapes:
+            cfg = synth.custom_config(f"llama3_8b_{nm}", M=M, K=K, N=N, bn=64)
+            lay = Layer(mq, torch, cfg)
+            p = lay.pack(cfg.k_blocks(10))
+            layers.append((lay, p, torch.empty((M, N), dtype=torch.bfloat16, device="cuda"),
+                           lay.w.to(torch.bfloat16), lay.x.to(torch.bfloat16)))
+            del lay.w
+
+        def ours(i):
+            for lay, p, y, _, _ in layers:
+                mq.quantize_act(lay.x, xq=lay.xq, sx=lay.sx)
+                mq.gemm_w4a4_residual(lay.xq, lay.sx, p["wq"], p["sw"], p["row_ptr"], p["col_idx"], p["rq"],
+                                      lay.cfg.K, bn=64, y=y)
+
+        def dense_only(i):
+            for lay, p, y, _, _ in layers:
+                mq.quantize_act(lay.x, xq=lay.xq, sx=lay.sx)
+                mq.gemm_w4a4_dense(lay.xq, lay.sx, p["wq"], p["sw"], lay.cfg.K, y=y)
+
+        def bf16(i):
+            for lay, p, y, wb, xb in layers:
+                torch.matmul(xb, wb.t(), out=y)
+        t_ours = _graph_time_us(torch, ours, 20)
+        t_dense = _graph_time_us(torch, dense_only, 20)
+        t_bf16 = _graph_time_us(torch, bf16, 20)
+        res["stack"].append({"M": M, "fused_us": round(t_ours, 2), "dense_us": round(t_dense, 2),
+                             "bf16_us": round(t_bf16, 2), "speedup_vs_bf16": round(t_bf16 / t_ours, 3),
+                             "overhead_vs_dense": round(t_ours / t_dense - 1, 4),
+                             "note": "weights of each layer read once per pass (7 layers, 218 MB of "
+                                     "bf16 weights; the Infinity Cache can hold part of the packed ones)"})
+        log(f"[sweep] stack M={M}: fused {t_ours:.1f} dense {t_dense:.1f} bf16 {t_bf16:.1f} us")
+        del layers
+        torch.cuda.empty_cache()
+    return res
 
 
 # --------------------------------------------------------------------------- main
@@ -419,31 +511,31 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=synth.BENCH_CONFIG, choices=sorted(synth.CONFIGS))
     ap.add_argument("--budget", type=int, default=None, help="residual budget in percent")
-    ap.add_argument("--gemm-calls", type=int, default=200)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--gemm-calls", type=int, default=200, help="calls per graph for the decode legs")
+    ap.add_argument("--cpu-rows", type=int, default=None, help="tokens in the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-gemm", action="store_true")
-    ap.add_argument("--no-calib", action="store_true")
+    ap.add_argument("--no-legs", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="batch sweep + layer stack, one JSON line")
     ap.add_argument("--pmc-pass", action="store_true",
-                    help="run a few steps and a copy of known size (for rocprofv3 --pmc), print nothing")
+                    help="a few GEMM calls and a copy of known size (for rocprofv3 --pmc), print nothing")
     ap.add_argument("--profile-summary", metavar="DB", help="print a rocprofv3 kernel-trace summary")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
-                    help="print HBM traffic per kernel from FETCH_SIZE and WRITE_SIZE passes")
+    ap.add_argument("--counters-summary", nargs="+", metavar="DB",
+                    help="print per-kernel counter means from rocprofv3 --pmc databases")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
     if args.profile_summary:
         print(profile_summary(args.profile_summary, args.title, " ; ".join(args.command)))
         return
-    if args.pmc_summary:
-        print(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.title, args.command))
+    if args.counters_summary:
+        print(counters_summary(args.counters_summary, args.title, args.command))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU leg in this build)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path has "
+              "no multi-GPU leg (each GPU would run the same kernel on its shard)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -451,96 +543,92 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
+    if args.sweep:
+        print(json.dumps(sweep(mq, torch, args.gemm_calls)), flush=True)
+        return
+
     cfg = synth.CONFIGS[args.workload]
     pct = cfg.default_budget if args.budget is None else args.budget
     k_blocks = cfg.k_blocks(pct)
-    inp = synth.make_inputs(cfg)
     if args.pmc_pass:
-        pmc_pass(mq, torch, cfg, inp, k_blocks)
+        pmc_pass(mq, torch, cfg, k_blocks)
         return
-    x_bytes = 2 if inp.X_bits is not None else 4
-    sb = step_bytes(cfg, k_blocks, x_bytes)
-    total_bytes = sum(sb.values())
 
-    st = bench_step(mq, torch, cfg, inp, k_blocks, args.steps, args.warmup)
-    kernels = {}
-    for n, us in st["us"].items():
-        gbs = sb[n] / us / 1e3
-        kernels[n] = {"us": round(us, 3), "bytes": sb[n], "GB/s": round(gbs, 1),
-                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
-    dom = max(st["us"], key=st["us"].get)
-    value = total_bytes / (st["gpu_ms"] * 1e-3) / 1e9
+    layer = Layer(mq, torch, cfg)
+    st = bench_step(mq, torch, layer, k_blocks, args.steps, args.warmup)
+    ops = gemm_ops(cfg, k_blocks)
+    value = ops / (st["gpu_ms"] * 1e-3) / 1e12
+    t = bench_variants(mq, torch, layer, k_blocks, max(10, min(args.gemm_calls, 30 if cfg.M > 32 else 200)))
+    gemm = leg_record(cfg, pct, k_blocks, t)
+    inp = layer.inp
+    del layer
+    torch.cuda.empty_cache()
 
-    gemm = None
-    if not args.no_gemm:
-        t = bench_gemm(mq, torch, cfg, inp, k_blocks, args.gemm_calls)
-        fb, db = gemm_bytes(cfg, k_blocks), gemm_bytes(cfg, k_blocks, residual=False)
-        fo, do = gemm_ops(cfg, k_blocks), gemm_ops(cfg, k_blocks, residual=False)
-        leg = lambda us, b, o: {"us": round(us, 3), "GB/s": round(b / us / 1e3, 1),
-                                "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
-                                "TOPS": round(o / us / 1e6, 3),
-                                "int8_frac": round(o / us / 1e6 / INT8_PEAK_TOPS, 5), "bytes": b,
-                                "ops": o}
-        gemm = {"fused": leg(t["fused"], fb, fo), "dense": leg(t["dense"], db, do),
-                "separate": leg(t["separate"], fb, fo),
-                "overhead_vs_dense": round(t["fused"] / t["dense"] - 1, 4),
-                "separate_overhead_vs_dense": round(t["separate"] / t["dense"] - 1, 4),
-                "residual_bytes_vs_base": round((fb - db) / (cfg.N * cfg.K // 2 + cfg.N * cfg.K // 64), 4),
-                "timing": "median of 5 replays of a HIP graph of %d back-to-back calls over rotated "
-                          "packed-weight copies, HIP events around each replay" % args.gemm_calls}
-
-    calib = None if args.no_calib else calibrate(torch)
+    legs = []
+    if not args.no_legs:
+        for name, budgets in LEGS:
+            c = synth.CONFIGS[name]
+            if c.name == cfg.name:
+                continue
+            lay = Layer(mq, torch, c)
+            rc = read_ceiling_us(torch, gemm_bytes(c, c.k_blocks(10)))
+            for b in budgets:
+                tb = bench_variants(mq, torch, lay, c.k_blocks(b), args.gemm_calls, bf16=(b == 10))
+                tb["read_ceiling_us"] = rc
+                rec = leg_record(c, b, c.k_blocks(b), tb)
+                legs.append(rec)
+                log(f"[bench] leg {c.name} {b}%: fused {tb['fused']:.2f} dense {tb['dense']:.2f} "
+                    f"separate {tb['separate']:.2f} us, overhead {rec['overhead_vs_dense']:.3f}, "
+                    f"{rec['fused']['hbm_frac']:.3f} of 8 TB/s")
+            del lay
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
-        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(cfg, inp, k_blocks, args.cpu_seconds, total_bytes)
+        rows = args.cpu_rows or min(cfg.M, 128)
+        log(f"[bench] CPU oracle baseline on {rows} tokens")
+        cpu = cpu_baseline(cfg, inp, k_blocks, rows)
 
-    dom_b = sb[dom]
-    traffic = None
-    if dom == "select_blocks":
-        t = traffic_from_profile(["mq::k_delta", "mq::k_rank", "mq::k_csr"],
-                                 os.path.join("dense_sparse_bit_amd", "csrc", "prep.hip"))
-        traffic = None if t is None else int(t)
+    kind = roofline_kind(cfg)
+    if kind == "mfma":
+        achieved, peak, unit = ops / st["gemm_us"] / 1e6, F8_PEAK_TOPS, "TOPS"
+    else:
+        achieved, peak, unit = gemm_bytes(cfg, k_blocks) / st["gemm_us"] / 1e3, HBM_PEAK_GBS, "GB/s"
+    kname = "k_gemm_prefill<true, false, 0>" if cfg.M > 32 else "k_gemm_decode"
     line = {
         "metric": METRIC,
         "value": round(value, 2),
-        "unit": "GB/s",
+        "unit": "TOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(st["gpu_ms"], 5),
         "wall_ms_per_step": round(st["wall_ms"], 5),
         "eager_ms_per_step": round(st["eager_ms"], 5),
-        "timing": "one replay of a HIP graph holding exactly `steps` steps (after `warmup` eager "
-                  "steps), HIP events on the launch stream, inputs rotated over %d HBM-resident "
-                  "copies; per-call figures: each call alone in its own graph" % st["copies"],
+        "timing": "one replay of a HIP graph holding exactly `steps` steps (after `warmup` eager steps), "
+                  "HIP events on the launch stream; weights rotated over %d HBM-resident packed copies "
+                  "(> 600 MB)" % st["copies"],
         "higher_is_better": True,
-        "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "int4 codes as fp8-e4m3 MFMA operands, fp32 accumulate (exact per-group integer sums)",
         "data": "synthetic, seeded (synth.py): random weights and activations with the shapes and "
-                "outlier structure of the workload",
-        "config": {"workload": f"{cfg.name}: M={cfg.M} K={cfg.K} N={cfg.N}, residual budget {pct}% "
-                               f"of {cfg.bn}x{cfg.bk} blocks ({k_blocks}/{(cfg.N // cfg.bn) * (cfg.K // cfg.bk)}), "
-                               f"int4 weights group 128, per-token int4 activations",
-                   "M": cfg.M, "K": cfg.K, "N": cfg.N, "bn": cfg.bn, "bk": cfg.bk,
-                   "budget_pct": pct, "k_blocks": k_blocks,
-                   "step": "hessian_diag -> select_blocks -> pack_weights -> quantize_act -> "
-                           "gemm_w4a4_residual"},
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(dom_b / st["us"][dom] / 1e3, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_b / st["us"][dom] / 1e3 / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "bytes_per_launch": dom_b, "us_per_launch": round(st["us"][dom], 3),
-                     "traffic_source": "profiles/select_blocks_llama3_8b_qo_hbm_traffic.txt (rocprofv3 "
-                                       "FETCH_SIZE and WRITE_SIZE passes, scaled by a copy of known size; "
-                                       "null when the kernel source changed since)"},
-        "cpu_baseline": None if cpu is None else {k: (round(v, 4) if isinstance(v, float) else v)
-                                                  for k, v in cpu.items() if k != "s_per_step"},
-        "step_kernels": kernels,
+                "outlier structure of the workload; no trained weights",
+        "config": {"workload": f"{cfg.name}: M={cfg.M} K={cfg.K} N={cfg.N}, residual budget {pct}% of "
+                               f"{cfg.bn}x{cfg.bk} blocks ({k_blocks}/{cfg.nb}), int4 weights group 128, "
+                               f"per-token int4 activations",
+                   "M": cfg.M, "K": cfg.K, "N": cfg.N, "bn": cfg.bn, "bk": cfg.bk, "budget_pct": pct,
+                   "k_blocks": k_blocks, "step": "quantize_act -> gemm_w4a4_residual"},
+        "roofline": {"kernel": kname, "bound": kind, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": traffic_from_profile("k_gemm_prefill<true, false" if cfg.M > 32 else "k_gemm_decode<"),
+                     "per_launch": {"ops": ops, "bytes": gemm_bytes(cfg, k_blocks), "us": round(st["gemm_us"], 3)},
+                     "hbm_GBs": round(gemm_bytes(cfg, k_blocks) / st["gemm_us"] / 1e3, 1),
+                     "traffic_source": TRAFFIC_SUMMARY + " (rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled "
+                                       "by a copy of known size; null when the kernel source changed since)"},
+        "step_kernels_us": {"quantize_act": round(st["quant_us"], 3), "gemm_w4a4_residual": round(st["gemm_us"], 3)},
         "gemm": gemm,
-        "calib": calib,
+        "legs": legs,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

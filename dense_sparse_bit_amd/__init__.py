@@ -36,10 +36,10 @@ _SIGS = {
     "mq_select_blocks": [_p, _p, _i64, _i64, _int, _int, _int, _i64, _p, _p, _p, _p, C.c_size_t, _p],
     "mq_pack_weights": [_p, _i64, _i64, _int, _int, _int, _p, _p, _i64, _p, _p, _p, _p],
     "mq_gemm_w4a4_residual": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
-                              _p, _int, _p, _p, C.c_size_t, _p],
-    "mq_gemm_w4a4_dense": [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p, _int, _p, _p, C.c_size_t, _p],
+                              _p, _int, _p, _p],
+    "mq_gemm_w4a4_dense": [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p, _int, _p, _p],
     "mq_gemm_residual_separate": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int,
-                                  _int, _p, _int, _p, _p, C.c_size_t, _p],
+                                  _int, _p, _int, _p, _p],
 }
 for _name, _args in _SIGS.items():
     getattr(_lib, _name).argtypes = _args
@@ -48,13 +48,10 @@ _lib.mq_status_string.argtypes = [C.c_int]
 _lib.mq_status_string.restype = C.c_char_p
 _lib.mq_version.argtypes = []
 _lib.mq_version.restype = C.c_int
-_lib.mq_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64]
-_lib.mq_gemm_workspace_bytes.restype = C.c_size_t
 _lib.mq_select_workspace_bytes.argtypes = [_i64, _i64, _int, _int]
 _lib.mq_select_workspace_bytes.restype = C.c_size_t
 
-EXPORTS = tuple(_SIGS) + ("mq_status_string", "mq_version", "mq_gemm_workspace_bytes",
-                          "mq_select_workspace_bytes")
+EXPORTS = tuple(_SIGS) + ("mq_status_string", "mq_version", "mq_select_workspace_bytes")
 
 
 class MQError(RuntimeError):
@@ -102,17 +99,56 @@ def _x_dtype(x: torch.Tensor) -> int:
 
 
 def _device_contig(t: torch.Tensor, name: str):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
+def _buf(t, name: str, nbytes: int, dtypes=None, align: int = 1):
+    """Checks a caller-supplied buffer before its pointer goes to the library:
+    type, dtype, size (at least nbytes), contiguity and alignment. The device is
+    checked last, for all operands of a call together (_on_device)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, needs at least {nbytes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if align > 1 and have and t.data_ptr() % align:
+        raise ValueError(f"{name} must be {align}-byte aligned")
+    return t
+
+
+def _on_device(**tensors):
+    """Every tensor a call hands to the library must live on the GPU."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+
+
+_U8 = (torch.uint8,)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+_SW = (torch.int16, torch.uint16, torch.float16) if hasattr(torch, "uint16") else (torch.int16, torch.float16)
+
+
+def _shape2(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    return int(t.shape[0]), int(t.shape[1])
+
+
 # --------------------------------------------------------------------------- a0
 def hessian_diag(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    M, K = _shape2(x, "x")
+    _x_dtype(x)
     _device_contig(x, "x")
-    M, K = x.shape
-    h = torch.empty(K, dtype=torch.float32, device=x.device) if out is None else out
+    h = torch.empty(K, dtype=torch.float32, device=x.device) if out is None else _buf(out, "h", 4 * K, _F32)
+    _on_device(x=x, h=h)
     _call("mq_hessian_diag", _ptr(x), _x_dtype(x), M, K, _ptr(h), _stream(stream))
     return h
 
@@ -121,60 +157,94 @@ def hessian_diag(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) 
 def quantize_act(x: torch.Tensor, xq: torch.Tensor | None = None, sx: torch.Tensor | None = None,
                  stream=None):
     """Returns (xq u8 [K/128][M][64], sx fp32 [M])."""
+    M, K = _shape2(x, "x")
+    _x_dtype(x)
     _device_contig(x, "x")
-    M, K = x.shape
     if xq is None:
         xq = torch.empty((K // GROUP, M, 64), dtype=torch.uint8, device=x.device)
+    else:
+        _buf(xq, "xq", M * K // 2, _U8, 16)
     if sx is None:
         sx = torch.empty(M, dtype=torch.float32, device=x.device)
+    else:
+        _buf(sx, "sx", 4 * M, _F32)
+    _on_device(x=x, xq=xq, sx=sx)
     _call("mq_quantize_act", _ptr(x), _x_dtype(x), M, K, _ptr(xq), _ptr(sx), _stream(stream))
     return xq, sx
 
 
 # --------------------------------------------------------------------------- a2
 def select_workspace(N: int, K: int, bn: int = 64, bk: int = BK, device="cuda"):
-    """Scratch for select_blocks (per-block ranks), so the call allocates nothing."""
+    """Scratch for select_blocks (per-block ranks, and the scores when they are not
+    returned), so the call allocates nothing."""
     n = int(_lib.mq_select_workspace_bytes(N, K, bn, bk))
-    return torch.empty(max(n, 4), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 8), dtype=torch.uint8, device=device)
 
 
 def select_blocks(w: torch.Tensor, h: torch.Tensor, k_blocks: int, bn: int = 64, group: int = GROUP,
-                  bk: int = BK, out=None, workspace=None, stream=None):
-    """Returns (row_ptr int32 [N/bn+1], col_idx int32 [k_blocks], delta fp64 [NB]).
+                  bk: int = BK, out=None, workspace=None, stream=None, return_delta: bool = True):
+    """Returns (row_ptr int32 [N/bn+1], col_idx int32 [k_blocks], delta fp64 [NB] or None).
     workspace: optional select_workspace(...) tensor; without it the library takes a
-    stream-ordered allocation for the call."""
+    stream-ordered allocation for the call. return_delta=False passes a NULL score
+    output (the scores stay in the scratch)."""
+    N, K = _shape2(w, "w")
+    if w.dtype != torch.float32 or h.dtype != torch.float32:
+        raise TypeError("w and h must be float32")
     _device_contig(w, "w")
-    _device_contig(h, "h")
-    N, K = w.shape
+    _buf(h, "h", 4 * K, _F32, 16)
+    if bn <= 0 or bk <= 0 or N % bn or K % bk:
+        raise ValueError(f"blocks {bn}x{bk} do not tile a {N}x{K} layer")
     nb = (N // bn) * (K // bk)
+    if not 0 <= k_blocks <= nb:
+        raise ValueError(f"k_blocks = {k_blocks} outside [0, {nb}]")
     if out is None:
         row_ptr = torch.empty(N // bn + 1, dtype=torch.int32, device=w.device)
         col_idx = torch.empty(max(k_blocks, 1), dtype=torch.int32, device=w.device)
-        delta = torch.empty(max(nb, 1), dtype=torch.float64, device=w.device)
+        delta = torch.empty(max(nb, 1), dtype=torch.float64, device=w.device) if return_delta else None
     else:
         row_ptr, col_idx, delta = out
-    ws = _ptr(workspace) if workspace is not None else None
-    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        _buf(row_ptr, "row_ptr", 4 * (N // bn + 1), _I32)
+        _buf(col_idx, "col_idx", 4 * k_blocks, _I32)
+        if delta is not None:
+            _buf(delta, "delta", 8 * nb, (torch.float64,))
+    ws, wsb = None, 0
+    if workspace is not None:
+        _buf(workspace, "workspace", 0, None, 8)
+        ws, wsb = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _on_device(w=w, h=h, row_ptr=row_ptr, col_idx=col_idx, delta=delta, workspace=workspace)
     _call("mq_select_blocks", _ptr(w), _ptr(h), N, K, group, bn, bk, k_blocks, _ptr(row_ptr),
           _ptr(col_idx), _ptr(delta), ws, wsb, _stream(stream))
-    return row_ptr, col_idx[:k_blocks], delta[:nb]
+    return row_ptr, col_idx[:k_blocks], (None if delta is None else delta[:nb])
 
 
 # --------------------------------------------------------------------------- a1 + a3
+def _csr_checks(row_ptr, col_idx, N, bn):
+    _buf(row_ptr, "row_ptr", 4 * (N // bn + 1), _I32)
+    if col_idx.numel():
+        _buf(col_idx, "col_idx", 4 * col_idx.numel(), _I32)
+    return int(col_idx.numel())
+
+
 def pack_weights(w: torch.Tensor, row_ptr: torch.Tensor, col_idx: torch.Tensor, bn: int = 64,
                  group: int = GROUP, bk: int = BK, out=None, stream=None):
     """Returns (wq u8 [N/16][G][1024], sw fp16-bits int16 [N/16][G4][16][4],
     rq u8 [nnz][bn][bk/2]) with G = K/128, G4 = ceil(G/4)."""
+    N, K = _shape2(w, "w")
+    if w.dtype != torch.float32:
+        raise TypeError("w must be float32")
     _device_contig(w, "w")
-    N, K = w.shape
-    nnz = int(col_idx.numel())
+    nnz = _csr_checks(row_ptr, col_idx, N, bn)
+    G = K // group
     if out is None:
-        G = K // group
         wq = torch.empty((N // 16, G, 1024), dtype=torch.uint8, device=w.device)
         sw = torch.empty((N // 16, (G + 3) // 4, 16, 4), dtype=torch.int16, device=w.device)
         rq = torch.empty((max(nnz, 1), bn, bk // 2), dtype=torch.uint8, device=w.device)
     else:
         wq, sw, rq = out
+        _buf(wq, "wq", N * K // 2, _U8, 16)
+        _buf(sw, "sw", 8 * N * ((G + 3) // 4), _SW, 8)
+        _buf(rq, "rq", nnz * bn * bk // 2, _U8, 16)
+    _on_device(w=w, row_ptr=row_ptr, col_idx=col_idx, wq=wq, sw=sw, rq=rq)
     _call("mq_pack_weights", _ptr(w), N, K, group, bn, bk, _ptr(row_ptr),
           _ptr(col_idx) if nnz else None, nnz, _ptr(wq), _ptr(sw), _ptr(rq) if nnz else None,
           _stream(stream))
@@ -190,70 +260,83 @@ def _y_dtype(dtype) -> int:
     raise TypeError(f"output must be float32 or bfloat16, got {dtype}")
 
 
-def _gemm_mn(sx, wq, K: int):
-    """(M, N) of a GEMM call: M tokens from sx, N outputs from the packed weight bytes."""
-    if K <= 0 or (wq.numel() * 2) % K:
+def _gemm_operands(xq, sx, wq, sw, K: int):
+    """(M, N) of a GEMM call, after checking the packed operands: M tokens from sx,
+    N outputs from the packed weight bytes."""
+    if K <= 0 or K % GROUP:
+        raise ValueError(f"K = {K} must be a positive multiple of {GROUP}")
+    _buf(sx, "sx", 0, _F32)
+    M = int(sx.numel())
+    if wq.numel() * 2 % K:
         raise ValueError(f"wq holds {wq.numel()} bytes, not a multiple of K/2 = {K // 2}")
-    return int(sx.numel()), int(wq.numel() * 2 // K)
+    N = int(wq.numel() * 2 // K)
+    if N % 16:
+        raise ValueError(f"wq describes N = {N} outputs, not a multiple of 16")
+    _buf(wq, "wq", N * K // 2, _U8, 16)
+    _buf(sw, "sw", 8 * N * ((K // GROUP + 3) // 4), _SW, 8)
+    _buf(xq, "xq", M * K // 2, _U8, 16)
+    return M, N
 
 
-def workspace_bytes(M: int, N: int, K: int) -> int:
-    """Device bytes of split-K partials the GEMM calls need for this shape."""
-    return int(_lib.mq_gemm_workspace_bytes(M, N, K))
+def _out_checks(y, M, N, out_dtype, device):
+    if y is None:
+        return torch.empty((M, N), dtype=out_dtype, device=device)
+    _buf(y, "y", M * N * (4 if y.dtype == torch.float32 else 2), (torch.float32, torch.bfloat16))
+    return y
 
 
-def workspace(M: int, N: int, K: int, device="cuda"):
-    """A workspace tensor for the GEMM calls of this shape (None if none is needed)."""
-    n = workspace_bytes(M, N, K)
-    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
-
-
-def _ws_args(workspace_t, M, N, K, device):
-    if workspace_t is None:
-        workspace_t = workspace(M, N, K, device)
-    if workspace_t is None:
-        return None, 0, None
-    return _ptr(workspace_t), workspace_t.numel() * workspace_t.element_size(), workspace_t
+def _dump_checks(acc_dump, M, N, K):
+    if acc_dump is not None:
+        _buf(acc_dump, "acc_dump", 4 * M * N * (K // GROUP), _I32)
 
 
 def gemm_w4a4_residual(xq, sx, wq, sw, row_ptr, col_idx, rq, K: int, bn: int = 64,
-                       out_dtype=torch.bfloat16, y=None, acc_dump=None, workspace=None,
-                       stream=None):
+                       out_dtype=torch.bfloat16, y=None, acc_dump=None, stream=None):
     """Fused dense + sparse-residual W4A4 GEMM. acc_dump: optional int32 [M][N][K/128]."""
-    M, N = _gemm_mn(sx, wq, K)
-    nnz = int(col_idx.numel())
-    if y is None:
-        y = torch.empty((M, N), dtype=out_dtype, device=wq.device)
-    wp, wb, _keep = _ws_args(workspace, M, N, K, wq.device)
+    M, N = _gemm_operands(xq, sx, wq, sw, K)
+    nnz = _csr_checks(row_ptr, col_idx, N, bn)
+    if nnz:
+        _buf(rq, "rq", nnz * bn * BK // 2, _U8, 16)
+    y = _out_checks(y, M, N, out_dtype, wq.device)
+    _dump_checks(acc_dump, M, N, K)
+    _on_device(xq=xq, sx=sx, wq=wq, sw=sw, row_ptr=row_ptr, col_idx=col_idx if nnz else None,
+               rq=rq if nnz else None, y=y, acc_dump=acc_dump)
     _call("mq_gemm_w4a4_residual", _ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(row_ptr),
           _ptr(col_idx) if nnz else None, _ptr(rq) if nnz else None, nnz, M, N, K, GROUP, bn, BK,
-          _ptr(y), _y_dtype(y.dtype), _ptr(acc_dump), wp, wb, _stream(stream))
+          _ptr(y), _y_dtype(y.dtype), _ptr(acc_dump), _stream(stream))
     return y
 
 
 def gemm_w4a4_dense(xq, sx, wq, sw, K: int, out_dtype=torch.bfloat16, y=None, acc_dump=None,
-                    workspace=None, stream=None):
-    M, N = _gemm_mn(sx, wq, K)
-    if y is None:
-        y = torch.empty((M, N), dtype=out_dtype, device=wq.device)
-    wp, wb, _keep = _ws_args(workspace, M, N, K, wq.device)
+                    stream=None):
+    """Dense-only W4A4 GEMM (the kernel the residual is fused into)."""
+    M, N = _gemm_operands(xq, sx, wq, sw, K)
+    y = _out_checks(y, M, N, out_dtype, wq.device)
+    _dump_checks(acc_dump, M, N, K)
+    _on_device(xq=xq, sx=sx, wq=wq, sw=sw, y=y, acc_dump=acc_dump)
     _call("mq_gemm_w4a4_dense", _ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), M, N, K, GROUP, _ptr(y),
-          _y_dtype(y.dtype), _ptr(acc_dump), wp, wb, _stream(stream))
+          _y_dtype(y.dtype), _ptr(acc_dump), _stream(stream))
     return y
 
 
 def gemm_residual_separate(xq, sx, wq, sw, row_ptr, col_idx, rq, K: int, bn: int = 64,
-                           out_dtype=torch.bfloat16, y=None, ws=None, workspace=None, stream=None):
-    M, N = _gemm_mn(sx, wq, K)
-    nnz = int(col_idx.numel())
-    if y is None:
-        y = torch.empty((M, N), dtype=out_dtype, device=wq.device)
+                           out_dtype=torch.bfloat16, y=None, ws=None, stream=None):
+    """The separate-kernel alternative: dense kernel to fp32 partials `ws`, then a
+    residual kernel that re-reads the activations and merges."""
+    M, N = _gemm_operands(xq, sx, wq, sw, K)
+    nnz = _csr_checks(row_ptr, col_idx, N, bn)
+    if nnz:
+        _buf(rq, "rq", nnz * bn * BK // 2, _U8, 16)
+    y = _out_checks(y, M, N, out_dtype, wq.device)
     if ws is None:
         ws = torch.empty((M, N), dtype=torch.float32, device=wq.device)
-    wp, wb, _keep = _ws_args(workspace, M, N, K, wq.device)
+    else:
+        _buf(ws, "ws", 4 * M * N, _F32)
+    _on_device(xq=xq, sx=sx, wq=wq, sw=sw, row_ptr=row_ptr, col_idx=col_idx if nnz else None,
+               rq=rq if nnz else None, y=y, ws=ws)
     _call("mq_gemm_residual_separate", _ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(row_ptr),
           _ptr(col_idx) if nnz else None, _ptr(rq) if nnz else None, nnz, M, N, K, GROUP, bn, BK,
-          _ptr(y), _y_dtype(y.dtype), _ptr(ws), wp, wb, _stream(stream))
+          _ptr(y), _y_dtype(y.dtype), _ptr(ws), _stream(stream))
     return y
 
 

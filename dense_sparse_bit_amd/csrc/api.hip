@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kVersion = 10000;   // 1.0.0
+constexpr int kVersion = 10100;   // 1.1.0
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -73,6 +73,19 @@ mq::GemmArgs make_args(const uint8_t* xq, const float* sx, const uint8_t* wq, co
     return a;
 }
 
+// argument checks of mq_select_blocks; the scratch (caller workspace or the
+// library's own) is checked by the caller of this helper
+int check_select(const float* w, const float* h, int64_t N, int64_t K, int group, int bn, int bk,
+                 int64_t k_blocks, const int32_t* row_ptr, const int32_t* col_idx) {
+    int rc = check_layer(N, K, group, bn, bk);
+    if (rc) return rc;
+    const int64_t nb = (N / bn) * (K / bk);
+    if (k_blocks < 0 || k_blocks > nb) return MQ_ERR_INVALID_ARG;
+    if (!w || !h || !row_ptr || (k_blocks > 0 && !col_idx) || !aligned16(w) || !aligned16(h))
+        return MQ_ERR_INVALID_ARG;
+    return MQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,22 +120,19 @@ int mq_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* x
 int mq_select_blocks(const float* w, const float* h, int64_t N, int64_t K, int group, int bn, int bk,
                      int64_t k_blocks, int32_t* row_ptr, int32_t* col_idx, double* delta,
                      void* workspace, size_t workspace_bytes, void* stream) {
-    int rc = check_layer(N, K, group, bn, bk);
+    int rc = check_select(w, h, N, K, group, bn, bk, k_blocks, row_ptr, col_idx);
     if (rc) return rc;
     const int64_t nb = (N / bn) * (K / bk);
-    if (k_blocks < 0 || k_blocks > nb) return MQ_ERR_INVALID_ARG;
-    if (!w || !h || !row_ptr || !delta || (k_blocks > 0 && !col_idx) || !aligned16(w) || !aligned16(h))
+    if (workspace && (workspace_bytes < mq::select_scratch_bytes(nb, delta == nullptr) ||
+                      (reinterpret_cast<uintptr_t>(workspace) & 7u)))
         return MQ_ERR_INVALID_ARG;
-    if (workspace && (workspace_bytes < static_cast<size_t>(nb) * sizeof(int32_t) ||
-                      (reinterpret_cast<uintptr_t>(workspace) & 3u)))
-        return MQ_ERR_INVALID_ARG;
-    return hip_status(mq::launch_select(w, h, N, K, bn, k_blocks, row_ptr, col_idx, delta,
-                                        static_cast<int32_t*>(workspace), static_cast<hipStream_t>(stream)));
+    return hip_status(mq::launch_select(w, h, N, K, bn, k_blocks, row_ptr, col_idx, delta, workspace,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 size_t mq_select_workspace_bytes(int64_t N, int64_t K, int bn, int bk) {
     if (check_layer(N, K, mq::kGroup, bn, bk)) return 0;
-    return static_cast<size_t>((N / bn) * (K / bk)) * sizeof(int32_t);
+    return mq::select_scratch_bytes((N / bn) * (K / bk), true);
 }
 
 int mq_pack_weights(const float* w, int64_t N, int64_t K, int group, int bn, int bk,
@@ -137,42 +147,10 @@ int mq_pack_weights(const float* w, int64_t N, int64_t K, int group, int bn, int
                                       static_cast<hipStream_t>(stream)));
 }
 
-size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    if (M <= 0 || N <= 0 || K <= 0 || N % 64 || K % mq::kGroup || K > 65536) return 0;
-    return mq::gemm_workspace_bytes(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
-}
-
-}  // extern "C"
-
-namespace {
-
-// Runs `launch(part)` with the split-K partial buffer the shape needs: the
-// caller's workspace if given (and large enough), else a stream-ordered
-// allocation released on the same stream.
-template <class F>
-int with_workspace(int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, hipStream_t st,
-                   F launch) {
-    const size_t need = mq::gemm_workspace_bytes(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
-    if (need == 0 || workspace) {
-        if (need > 0 && workspace_bytes < need) return MQ_ERR_INVALID_ARG;
-        return hip_status(launch(static_cast<float*>(workspace)));
-    }
-    float* tmp = nullptr;
-    if (hipMallocAsync(reinterpret_cast<void**>(&tmp), need, st) != hipSuccess) return MQ_ERR_HIP;
-    const hipError_t e = launch(tmp);
-    const hipError_t f = hipFreeAsync(tmp, st);
-    return (e == hipSuccess && f == hipSuccess) ? MQ_OK : MQ_ERR_HIP;
-}
-
-}  // namespace
-
-extern "C" {
-
 int mq_gemm_w4a4_residual(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint16_t* sw,
                           const int32_t* row_ptr, const int32_t* col_idx, const uint8_t* rq,
                           int64_t nnz, int64_t M, int64_t N, int64_t K, int group, int bn, int bk,
-                          void* y, int y_dtype, int32_t* acc_dump, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          void* y, int y_dtype, int32_t* acc_dump, void* stream) {
     int rc = check_gemm(xq, sx, wq, sw, M, N, K, group, bn, bk, y, y_dtype);
     if (rc) return rc;
     rc = check_csr(row_ptr, col_idx, rq, nnz, N, K, bn, bk);
@@ -180,29 +158,25 @@ int mq_gemm_w4a4_residual(const uint8_t* xq, const float* sx, const uint8_t* wq,
     if (M == 0) return MQ_OK;
     const mq::GemmArgs a = make_args(xq, sx, wq, sw, row_ptr, col_idx, rq, nnz, M, N, K, bn, y, y_dtype,
                                      acc_dump, nullptr);
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    return with_workspace(M, N, K, workspace, workspace_bytes, st,
-                          [&](float* part) { return mq::launch_gemm(a, mq::GemmKind::Fused, part, st); });
+    return hip_status(mq::launch_gemm(a, mq::GemmKind::Fused, static_cast<hipStream_t>(stream)));
 }
 
 int mq_gemm_w4a4_dense(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint16_t* sw,
                        int64_t M, int64_t N, int64_t K, int group, void* y, int y_dtype,
-                       int32_t* acc_dump, void* workspace, size_t workspace_bytes, void* stream) {
+                       int32_t* acc_dump, void* stream) {
     int rc = check_gemm(xq, sx, wq, sw, M, N, K, group, 64, mq::kBk, y, y_dtype);
     if (rc) return rc;
     if (M == 0) return MQ_OK;
     const mq::GemmArgs a = make_args(xq, sx, wq, sw, nullptr, nullptr, nullptr, 0, M, N, K, 64, y, y_dtype,
                                      acc_dump, nullptr);
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    return with_workspace(M, N, K, workspace, workspace_bytes, st,
-                          [&](float* part) { return mq::launch_gemm(a, mq::GemmKind::Dense, part, st); });
+    return hip_status(mq::launch_gemm(a, mq::GemmKind::Dense, static_cast<hipStream_t>(stream)));
 }
 
 int mq_gemm_residual_separate(const uint8_t* xq, const float* sx, const uint8_t* wq,
                               const uint16_t* sw, const int32_t* row_ptr, const int32_t* col_idx,
                               const uint8_t* rq, int64_t nnz, int64_t M, int64_t N, int64_t K,
                               int group, int bn, int bk, void* y, int y_dtype, float* ws,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              void* stream) {
     int rc = check_gemm(xq, sx, wq, sw, M, N, K, group, bn, bk, y, y_dtype);
     if (rc) return rc;
     rc = check_csr(row_ptr, col_idx, rq, nnz, N, K, bn, bk);
@@ -212,10 +186,9 @@ int mq_gemm_residual_separate(const uint8_t* xq, const float* sx, const uint8_t*
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const mq::GemmArgs a = make_args(xq, sx, wq, sw, row_ptr, col_idx, rq, nnz, M, N, K, bn, y, y_dtype,
                                      nullptr, ws);
-    return with_workspace(M, N, K, workspace, workspace_bytes, st, [&](float* part) {
-        hipError_t e = mq::launch_gemm(a, mq::GemmKind::DenseToWorkspace, part, st);
-        return e != hipSuccess ? e : mq::launch_residual_merge(a, st);
-    });
+    hipError_t e = mq::launch_gemm(a, mq::GemmKind::DenseToWorkspace, st);
+    if (e == hipSuccess) e = mq::launch_residual_merge(a, st);
+    return hip_status(e);
 }
 
 }  // extern "C"

@@ -568,13 +568,7 @@ DecodePlan plan_decode(int M, int N, int K) {
     return DecodePlan{nw};
 }
 
-size_t gemm_workspace_bytes(int M, int N, int K) {
-    (void)M; (void)N; (void)K;
-    return 0;
-}
-
-hipError_t launch_gemm(const GemmArgs& a, GemmKind kind, float* part, hipStream_t st) {
-    (void)part;
+hipError_t launch_gemm(const GemmArgs& a, GemmKind kind, hipStream_t st) {
     const bool dump = a.acc_dump != nullptr;
     switch (kind) {
         case GemmKind::Fused:

@@ -168,10 +168,6 @@ __device__ __forceinline__ v4f mfma_f8(v8i a, v8i b, v4f c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint4 ldg16(const uint8_t* p) {
-    return *reinterpret_cast<const uint4*>(p);
-}
-
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // ---- raw buffer loads ------------------------------------------------------

@@ -29,20 +29,24 @@ struct DecodePlan {
     int nw;
 };
 DecodePlan plan_decode(int M, int N, int K);
-// device workspace the GEMM of this shape needs (0 if none)
-size_t gemm_workspace_bytes(int M, int N, int K);
+// scratch bytes of the selection: per-block ranks (4 nb, padded to 8) and, when the
+// caller passes no delta output, the fp64 scores (8 nb)
+inline size_t select_scratch_bytes(int64_t nb, bool scores) {
+    const size_t ranks = (static_cast<size_t>(nb) * 4 + 7) & ~static_cast<size_t>(7);
+    return ranks + (scores ? static_cast<size_t>(nb) * 8 : 0);
+}
 
 hipError_t launch_hessian(const void* x, int bf16, int64_t M, int64_t K, float* h, hipStream_t st);
 hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, uint8_t* xq, float* sx,
                             hipStream_t st);
-// rank_ws: nb int32 of scratch, or null for a stream-ordered allocation
+// scratch: select_scratch_bytes(nb, delta == null) bytes, or null for a stream-ordered allocation
 hipError_t launch_select(const float* w, const float* h, int64_t N, int64_t K, int bn,
                          int64_t k_blocks, int32_t* row_ptr, int32_t* col_idx, double* delta,
-                         int32_t* rank_ws, hipStream_t st);
+                         void* scratch, hipStream_t st);
 hipError_t launch_pack(const float* w, int64_t N, int64_t K, int bn, const int32_t* row_ptr,
                        const int32_t* col_idx, int64_t nnz, uint8_t* wq, uint16_t* sw, uint8_t* rq,
                        hipStream_t st);
-hipError_t launch_gemm(const GemmArgs& a, GemmKind kind, float* part, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs& a, GemmKind kind, hipStream_t st);
 hipError_t launch_residual_merge(const GemmArgs& a, hipStream_t st);
 
 }  // namespace mq

@@ -569,24 +569,27 @@ hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, uint8
 
 hipError_t launch_select(const float* w, const float* h, int64_t N, int64_t K, int bn,
                          int64_t k_blocks, int32_t* row_ptr, int32_t* col_idx, double* delta,
-                         int32_t* rank_ws, hipStream_t st) {
+                         void* scratch, hipStream_t st) {
     const int64_t nbr = N / bn, nbc = K / kBk, nb = nbr * nbc;
-    int32_t* rank = rank_ws;
+    void* buf = scratch;
     hipError_t err = hipSuccess;
-    if (!rank) {
-        err = hipMallocAsync(reinterpret_cast<void**>(&rank), static_cast<size_t>(nb) * sizeof(int32_t), st);
+    if (!buf) {
+        err = hipMallocAsync(&buf, select_scratch_bytes(nb, delta == nullptr), st);
         if (err != hipSuccess) return err;
     }
+    int32_t* rank = static_cast<int32_t*>(buf);
+    double* score = delta ? delta
+                          : reinterpret_cast<double*>(static_cast<char*>(buf) + select_scratch_bytes(nb, false));
     // about four workgroups per CU: each walks nbr / P block rows of one group
     const int64_t G = K / kGroup;
     const int64_t P = std::max<int64_t>(1, std::min<int64_t>(nbr, (1024 + G - 1) / G));
     k_delta<<<dim3(static_cast<unsigned>(P), static_cast<unsigned>(G)), dim3(128), 0, st>>>(
-        w, h, K, bn, static_cast<int>(nbr), delta, rank);
+        w, h, K, bn, static_cast<int>(nbr), score, rank);
     err = hipGetLastError();
     const unsigned nblk = static_cast<unsigned>((nb + 255) / 256);
     if (err == hipSuccess) {
         k_rank<<<dim3(nblk, static_cast<unsigned>((nb + kRankSlice - 1) / kRankSlice)), dim3(256), 0, st>>>(
-            delta, nb, rank);
+            score, nb, rank);
         err = hipGetLastError();
     }
     if (err == hipSuccess) {
@@ -594,8 +597,8 @@ hipError_t launch_select(const float* w, const float* h, int64_t N, int64_t K, i
                                               static_cast<int>(nbr), static_cast<int>(k_blocks), row_ptr, col_idx);
         err = hipGetLastError();
     }
-    if (rank_ws) return err;
-    const hipError_t ferr = hipFreeAsync(rank, st);
+    if (scratch) return err;
+    const hipError_t ferr = hipFreeAsync(buf, st);
     return err != hipSuccess ? err : ferr;
 }
 

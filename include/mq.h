@@ -105,16 +105,19 @@ int mq_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* x
  *   row_ptr: int32 [N/bn + 1], col_idx: int32 [k_blocks] (column-block index,
  *   ascending within a row), delta: fp64 [NB] with NB = (N/bn)*(K/bk).
  * w: fp32 [N][K], h: fp32 [K]. 0 <= k_blocks <= NB.
- * workspace: device scratch of at least mq_select_workspace_bytes(N, K, bn, bk) bytes
- * (4 * NB, 4-byte aligned; the per-block ranks), or NULL: the call then takes a
- * stream-ordered allocation (hipMallocAsync) and releases it on the same stream.
- * Calls sharing one workspace must be ordered on one stream.
+ * delta may be NULL (the scores are then kept in the workspace and not returned).
+ * workspace: device scratch of at least mq_select_workspace_bytes(N, K, bn, bk) bytes,
+ * 8-byte aligned (the per-block ranks, 4 * NB bytes, and when delta is NULL the
+ * scores, 8 * NB more), or NULL: the call then takes a stream-ordered allocation
+ * (hipMallocAsync) and releases it on the same stream. Calls sharing one
+ * workspace must be ordered on one stream.
  */
 int mq_select_blocks(const float* w, const float* h, int64_t N, int64_t K, int group, int bn,
                      int bk, int64_t k_blocks, int32_t* row_ptr, int32_t* col_idx,
                      double* delta, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes mq_select_blocks needs for this shape (0 for an unsupported shape). */
+/* Workspace bytes mq_select_blocks needs for this shape with delta == NULL (12 * NB;
+   4 * NB suffice when delta is given); 0 for an unsupported shape. */
 size_t mq_select_workspace_bytes(int64_t N, int64_t K, int bn, int bk);
 
 /*
@@ -148,21 +151,13 @@ int mq_pack_weights(const float* w, int64_t N, int64_t K, int group, int bn, int
  * acc_dump: NULL, or int32 [M][N][K/group] receiving T (a debug build of the same
  * kernel; production calls pass NULL). Indices outside the CSR ranges are ignored,
  * so a malformed list gives wrong values, never an out-of-bounds access.
- * workspace: device scratch of at least mq_gemm_workspace_bytes(M, N, K) bytes, or
- * NULL: the call then takes a stream-ordered allocation (hipMallocAsync) and
- * releases it on the same stream. The current kernels need none (the function
- * returns 0 for every shape), so NULL costs nothing. A workspace smaller than
- * required returns MQ_ERR_INVALID_ARG. Calls sharing one workspace must be
- * ordered on one stream.
+ * The call allocates nothing and needs no scratch memory.
  */
 int mq_gemm_w4a4_residual(const uint8_t* xq, const float* sx, const uint8_t* wq,
                           const uint16_t* sw, const int32_t* row_ptr, const int32_t* col_idx,
                           const uint8_t* rq, int64_t nnz, int64_t M, int64_t N, int64_t K,
                           int group, int bn, int bk, void* y, int y_dtype, int32_t* acc_dump,
-                          void* workspace, size_t workspace_bytes, void* stream);
-
-/* Workspace bytes the GEMM calls below need for this shape (0: none). */
-size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+                          void* stream);
 
 /*
  * Dense-only 4-bit GEMM: the same kernel with the residual path compiled out
@@ -172,7 +167,7 @@ size_t mq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  */
 int mq_gemm_w4a4_dense(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint16_t* sw,
                        int64_t M, int64_t N, int64_t K, int group, void* y, int y_dtype,
-                       int32_t* acc_dump, void* workspace, size_t workspace_bytes, void* stream);
+                       int32_t* acc_dump, void* stream);
 
 /*
  * The separate-kernel alternative that Methodology 3 argues against: the dense
@@ -186,7 +181,7 @@ int mq_gemm_residual_separate(const uint8_t* xq, const float* sx, const uint8_t*
                               const uint16_t* sw, const int32_t* row_ptr, const int32_t* col_idx,
                               const uint8_t* rq, int64_t nnz, int64_t M, int64_t N, int64_t K,
                               int group, int bn, int bk, void* y, int y_dtype, float* ws,
-                              void* workspace, size_t workspace_bytes, void* stream);
+                              void* stream);
 
 #ifdef __cplusplus
 }

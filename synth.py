@@ -86,7 +86,7 @@ CONFIGS = {
 }
 
 # The workload the benchmark line is quoted on.
-BENCH_CONFIG = "llama3_8b_qo"
+BENCH_CONFIG = "qwen3_14b_prefill"
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:

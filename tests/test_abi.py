@@ -34,7 +34,7 @@ def mq():
 def test_header_declares_the_boundary():
     names = _declared()
     for fn in ["mq_quantize_act", "mq_pack_weights", "mq_select_blocks", "mq_gemm_w4a4_residual",
-               "mq_gemm_workspace_bytes", "mq_select_workspace_bytes",
+               "mq_select_workspace_bytes",
                "mq_hessian_diag", "mq_gemm_w4a4_dense", "mq_gemm_residual_separate",
                "mq_status_string", "mq_version"]:
         assert fn in names
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(mq):
     for fn in _declared():
         assert hasattr(lib, fn), fn
     assert set(_declared()) == set(mq.EXPORTS)
-    assert mq.version() == 10000
+    assert mq.version() == 10100
     for s in (0, -1, -2, -3):
         assert mq.status_string(s)
 
@@ -69,7 +69,7 @@ def _gemm(lib, **kw):
     a.update(kw)
     return lib.mq_gemm_w4a4_residual(a["xq"], a["sx"], a["wq"], a["sw"], a["row_ptr"], a["col_idx"],
                                      a["rq"], a["nnz"], a["M"], a["N"], a["K"], a["group"], a["bn"],
-                                     a["bk"], a["y"], a["y_dtype"], a["dump"], None, 0, a["stream"])
+                                     a["bk"], a["y"], a["y_dtype"], a["dump"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -100,24 +100,23 @@ def test_preparation_calls_reject_bad_arguments(lib_nogpu):
     assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, nb + 1, FAKE, FAKE, FAKE, None, 0, None) == -1
     assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, -1, FAKE, FAKE, FAKE, None, 0, None) == -1
     assert lib.mq_select_blocks(FAKE, FAKE, 512, 500, 128, 64, 64, 3, FAKE, FAKE, FAKE, None, 0, None) == -2
-    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, 3, FAKE, FAKE, None, None, 0, None) == -1
-    # a workspace smaller than the per-block ranks, or misaligned, is rejected before any launch
-    assert lib.mq_select_workspace_bytes(512, 512, 64, 64) == 4 * nb
+    # a workspace smaller than the scratch the call needs, or misaligned, is rejected before
+    # any launch: 4 * NB bytes of ranks, plus 8 * NB of scores when delta is NULL
+    assert lib.mq_select_workspace_bytes(512, 512, 64, 64) == 12 * nb
     assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, 3, FAKE, FAKE, FAKE, FAKE,
                                 4 * nb - 1, None) == -1
-    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, 3, FAKE, FAKE, FAKE, FAKE + 2,
+    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, 3, FAKE, FAKE, None, FAKE,
+                                12 * nb - 1, None) == -1
+    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, 3, FAKE, FAKE, FAKE, FAKE + 4,
                                 4 * nb, None) == -1
+    assert lib.mq_select_blocks(FAKE, FAKE, 512, 512, 128, 64, 64, 3, None, FAKE, FAKE, None, 0, None) == -1
     assert lib.mq_pack_weights(FAKE, 512, 512, 128, 64, 64, None, FAKE, 3, FAKE, FAKE, FAKE, None) == -1
     assert lib.mq_pack_weights(FAKE + 4, 512, 512, 128, 64, 64, FAKE, FAKE, 3, FAKE, FAKE, FAKE, None) == -1
-    assert lib.mq_gemm_w4a4_dense(FAKE, FAKE, FAKE, FAKE, 4, 512, 320, 128, FAKE, 0, None, None, 0,
-                                  None) == -2
+    assert lib.mq_gemm_w4a4_dense(FAKE, FAKE, FAKE, FAKE, 4, 512, 320, 128, FAKE, 0, None, None) == -2
     assert lib.mq_gemm_residual_separate(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 4, 512, 512,
-                                         128, 64, 64, FAKE, 0, None, None, 0, None) == -1
+                                         128, 64, 64, FAKE, 0, None, None) == -1
     # the packed activation layout is group-major, so K must be a multiple of 128
     assert lib.mq_quantize_act(FAKE, 1, 4, 130, FAKE, FAKE, None) == -2
-    # the current GEMM kernels need no workspace for any supported shape
-    for M, N, K in [(1, 64, 128), (16, 4096, 4096), (32, 5120, 25600), (2048, 17408, 5120)]:
-        assert lib.mq_gemm_workspace_bytes(M, N, K) == 0
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
@@ -134,3 +133,62 @@ def test_binding_fails_loudly_without_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import dense_sparse_bit_amd"], cwd=str(tmp_path),
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0 and "libmq.so is missing" in r.stderr
+
+
+# --------------------------------------------------------------------------- binding checks
+def test_binding_rejects_bad_buffers(mq):
+    """The Python binding checks every caller-supplied tensor (type, dtype, size,
+    contiguity, device) before a pointer reaches the library. Run on host tensors:
+    each call must fail in the binding, never launch."""
+    import torch
+    M, N, K = 4, 64, 256
+    xq = torch.zeros((K // 128, M, 64), dtype=torch.uint8)
+    sx = torch.zeros(M, dtype=torch.float32)
+    wq = torch.zeros((N // 16, K // 128, 1024), dtype=torch.uint8)
+    sw = torch.zeros((N // 16, 1, 16, 4), dtype=torch.int16)
+    rp = torch.zeros(N // 64 + 1, dtype=torch.int32)
+    ci = torch.zeros(2, dtype=torch.int32)
+    rq = torch.zeros((2, 64, 32), dtype=torch.uint8)
+    none = torch.zeros(0, dtype=torch.int32)
+    # too-small outputs and dumps
+    with pytest.raises(ValueError, match="y holds"):
+        mq.gemm_w4a4_residual(xq, sx, wq, sw, rp, none, none, K, y=torch.zeros((M, N - 1)))
+    with pytest.raises(ValueError, match="acc_dump holds"):
+        mq.gemm_w4a4_dense(xq, sx, wq, sw, K, y=torch.zeros((M, N)),
+                           acc_dump=torch.zeros((M, N, 1), dtype=torch.int32))
+    with pytest.raises(ValueError, match="ws holds"):
+        mq.gemm_residual_separate(xq, sx, wq, sw, rp, none, none, K, ws=torch.zeros((M, N - 1)))
+    # too-small packed inputs, wrong dtypes
+    with pytest.raises(ValueError, match="xq holds"):
+        mq.gemm_w4a4_dense(xq[:, :2], sx, wq, sw, K)
+    with pytest.raises(ValueError, match="sw holds"):
+        mq.gemm_w4a4_dense(xq, sx, wq, sw[:2], K)
+    with pytest.raises(ValueError, match="rq holds"):
+        mq.gemm_w4a4_residual(xq, sx, wq, sw, rp, ci, rq[:1], K)
+    with pytest.raises(ValueError, match="row_ptr holds"):
+        mq.gemm_w4a4_residual(xq, sx, wq, sw, rp[:1], ci, rq, K)
+    with pytest.raises(TypeError, match="sx must have dtype"):
+        mq.gemm_w4a4_dense(xq, sx.double(), wq, sw, K)
+    with pytest.raises(TypeError, match="y must have dtype"):
+        mq.gemm_w4a4_dense(xq, sx, wq, sw, K, y=torch.zeros((M, N), dtype=torch.float64))
+    with pytest.raises(ValueError, match="multiple of 128"):
+        mq.gemm_w4a4_dense(xq, sx, wq, sw, 200)
+    # a strided (non-contiguous) output of the right size
+    with pytest.raises(ValueError, match="contiguous"):
+        mq.gemm_w4a4_dense(xq, sx, wq, sw, K, y=torch.zeros((N, M)).t())
+    # host tensors of the right size never reach the library
+    with pytest.raises(ValueError, match="device tensor"):
+        mq.gemm_w4a4_dense(xq, sx, wq, sw, K, y=torch.zeros((M, N)))
+    x = torch.zeros((M, K), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="xq holds"):
+        mq.quantize_act(x, xq=torch.zeros(M * K // 2 - 1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="sx holds"):
+        mq.quantize_act(x, sx=torch.zeros(M - 1))
+    w = torch.zeros((N, K), dtype=torch.float32)
+    h = torch.zeros(K, dtype=torch.float32)
+    with pytest.raises(ValueError, match="k_blocks"):
+        mq.select_blocks(w, h, (N // 64) * (K // 64) + 1)
+    with pytest.raises(ValueError, match="col_idx holds"):
+        mq.select_blocks(w, h, 3, out=(rp, ci, torch.zeros(4, dtype=torch.float64)))
+    with pytest.raises(ValueError, match="wq holds"):
+        mq.pack_weights(w, rp, ci, out=(wq[:1], sw, rq))

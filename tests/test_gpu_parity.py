@@ -103,12 +103,16 @@ def _run_gpu(mq, inp, k_blocks, out_dtype):
     w = _to_dev(inp.W)
     h = mq.hessian_diag(x)
     rp, ci, delta = mq.select_blocks(w, h, k_blocks, bn=cfg.bn)
+    # the same selection with no score output (the scores stay in the library's scratch)
+    rp2, ci2, none = mq.select_blocks(w, h, k_blocks, bn=cfg.bn, return_delta=False)
+    assert none is None
     wq, sw, rq = mq.pack_weights(w, rp, ci, bn=cfg.bn)
     xq, sx = mq.quantize_act(x)
     dump = torch.empty((cfg.M, cfg.N, cfg.K // 128), dtype=torch.int32, device="cuda")
     y = mq.gemm_w4a4_residual(xq, sx, wq, sw, rp, ci, rq, cfg.K, bn=cfg.bn, out_dtype=out_dtype,
                               acc_dump=dump)
     torch.cuda.synchronize()
+    assert torch.equal(rp2, rp) and torch.equal(ci2, ci), "selection without score output differs"
     return dict(h=h, row_ptr=rp, col_idx=ci, delta=delta, wq=wq, sw=sw, rq=rq, xq=xq, sx=sx, y=y,
                 dump=dump, w=w, x=x)
 
@@ -138,22 +142,38 @@ def _check(mq, orc, inp, k_blocks, out_dtype_name="bf16", rows=None, check_varia
     np.testing.assert_array_equal(_np(dump).astype(np.int64), ref["T"])
     y = _np(g["y"])[sel]
     err = rel_err(y, ref["y"])
-    say(f"[parity] {cfg.name} y max rel err {err:.3e}")
+    say(f"[parity] {cfg.name} y max rel err {err:.3e} (debug build)")
     assert err <= Y_TOL[out_dtype_name]
+    # the production build (no dump), the kernel the benchmark times: the same
+    # bits as the debug build, hence the same error against the oracle
+    bits = (lambda t: t.view(torch.int16)) if out_dtype == torch.bfloat16 else (lambda t: t.view(torch.int32))
+    yp = mq.gemm_w4a4_residual(g["xq"], g["sx"], g["wq"], g["sw"], g["row_ptr"], g["col_idx"], g["rq"],
+                               cfg.K, bn=cfg.bn, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    err_p = rel_err(_np(yp)[sel], ref["y"])
+    say(f"[parity] {cfg.name} y max rel err {err_p:.3e} (production build)")
+    assert err_p <= Y_TOL[out_dtype_name]
+    assert torch.equal(bits(yp), bits(g["y"])), "production and debug builds differ"
     if check_variants:
         # dense-only kernel: T = 14 P, and y equals the fused kernel with no residual
         ddump = torch.empty_like(g["dump"])
         yd = mq.gemm_w4a4_dense(g["xq"], g["sx"], g["wq"], g["sw"], cfg.K, out_dtype=out_dtype,
                                 acc_dump=ddump)
+        ydp = mq.gemm_w4a4_dense(g["xq"], g["sx"], g["wq"], g["sw"], cfg.K, out_dtype=out_dtype)
         empty = torch.zeros(cfg.N // cfg.bn + 1, dtype=torch.int32, device="cuda")
         none = torch.empty(0, dtype=torch.int32, device="cuda")
         y0 = mq.gemm_w4a4_residual(g["xq"], g["sx"], g["wq"], g["sw"], empty, none, none, cfg.K,
                                    bn=cfg.bn, out_dtype=out_dtype)
+        y0d = mq.gemm_w4a4_residual(g["xq"], g["sx"], g["wq"], g["sw"], empty, none, none, cfg.K,
+                                    bn=cfg.bn, out_dtype=out_dtype, acc_dump=torch.empty_like(g["dump"]))
         torch.cuda.synchronize()
-        assert torch.equal(yd.view(torch.int16) if out_dtype == torch.bfloat16 else yd.view(torch.int32),
-                           y0.view(torch.int16) if out_dtype == torch.bfloat16 else y0.view(torch.int32))
+        assert torch.equal(bits(yd), bits(y0))
+        assert torch.equal(bits(ydp), bits(yd)), "dense production and debug builds differ"
+        assert torch.equal(bits(y0d), bits(y0))
         dd = ddump if rows is None else ddump[torch.as_tensor(rows, device="cuda")]
         np.testing.assert_array_equal(_np(dd).astype(np.int64), 14 * ref["P"].astype(np.int64))
+        if k_blocks == 0:
+            assert torch.equal(bits(yp), bits(ydp)), "an empty residual must give the dense kernel's bits"
         # the separate-kernel alternative computes the same y within tolerance
         ys = mq.gemm_residual_separate(g["xq"], g["sx"], g["wq"], g["sw"], g["row_ptr"], g["col_idx"],
                                        g["rq"], cfg.K, bn=cfg.bn, out_dtype=out_dtype)
