@@ -34,6 +34,7 @@ _SIGS = {
     "mq_hessian_diag": [_p, _int, _i64, _i64, _p, _p],
     "mq_quantize_act": [_p, _int, _i64, _i64, _p, _p, _p],
     "mq_select_blocks": [_p, _p, _i64, _i64, _int, _int, _int, _i64, _p, _p, _p, _p, C.c_size_t, _p],
+    "mq_select_blocks_noalloc": [_p, _p, _i64, _i64, _int, _int, _int, _i64, _p, _p, _p, _p],
     "mq_pack_weights": [_p, _i64, _i64, _int, _int, _int, _p, _p, _i64, _p, _p, _p, _p],
     "mq_gemm_w4a4_residual": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
                               _p, _int, _p, _p],
@@ -214,6 +215,36 @@ def select_blocks(w: torch.Tensor, h: torch.Tensor, k_blocks: int, bn: int = 64,
     _on_device(w=w, h=h, row_ptr=row_ptr, col_idx=col_idx, delta=delta, workspace=workspace)
     _call("mq_select_blocks", _ptr(w), _ptr(h), N, K, group, bn, bk, k_blocks, _ptr(row_ptr),
           _ptr(col_idx), _ptr(delta), ws, wsb, _stream(stream))
+    return row_ptr, col_idx[:k_blocks], (None if delta is None else delta[:nb])
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20     # MQ_NOALLOC_SCRATCH_BYTES
+
+
+def select_blocks_noalloc(w: torch.Tensor, h: torch.Tensor, k_blocks: int, row_ptr: torch.Tensor,
+                          col_idx: torch.Tensor, delta: torch.Tensor | None = None, bn: int = 64,
+                          group: int = GROUP, bk: int = BK, stream=None):
+    """select_blocks into caller-supplied outputs with no allocation at all (the
+    library's static scratch): for code under graph capture or in loops that must
+    not allocate. delta=None leaves the scores in the scratch. Calls that overlap on
+    one GPU race (one scratch array per GPU)."""
+    N, K = _shape2(w, "w")
+    if w.dtype != torch.float32 or h.dtype != torch.float32:
+        raise TypeError("w and h must be float32")
+    _device_contig(w, "w")
+    _buf(h, "h", 4 * K, _F32, 16)
+    if bn <= 0 or bk <= 0 or N % bn or K % bk:
+        raise ValueError(f"blocks {bn}x{bk} do not tile a {N}x{K} layer")
+    nb = (N // bn) * (K // bk)
+    if not 0 <= k_blocks <= nb:
+        raise ValueError(f"k_blocks = {k_blocks} outside [0, {nb}]")
+    _buf(row_ptr, "row_ptr", 4 * (N // bn + 1), _I32)
+    _buf(col_idx, "col_idx", 4 * k_blocks, _I32)
+    if delta is not None:
+        _buf(delta, "delta", 8 * nb, (torch.float64,))
+    _on_device(w=w, h=h, row_ptr=row_ptr, col_idx=col_idx, delta=delta)
+    _call("mq_select_blocks_noalloc", _ptr(w), _ptr(h), N, K, group, bn, bk, k_blocks, _ptr(row_ptr),
+          _ptr(col_idx), _ptr(delta), _stream(stream))
     return row_ptr, col_idx[:k_blocks], (None if delta is None else delta[:nb])
 
 

@@ -2,9 +2,17 @@
 // Declarations and the meaning of every argument are in include/mq.h.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/mq.h"
 #include "mq_device.h"
 #include "mq_internal.h"
+
+// Static scratch of mq_select_blocks_noalloc, one copy per GPU. In host code
+// `scratch` names a host-side stand-in, not device memory: its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current) and
+// only that address is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[MQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -86,6 +94,23 @@ int check_select(const float* w, const float* h, int64_t N, int64_t K, int group
     return MQ_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's address of `scratch` (looked up on first use), or null on error
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -96,6 +121,7 @@ const char* mq_status_string(int status) {
         case MQ_ERR_INVALID_ARG: return "invalid argument (null pointer, size, alignment or count)";
         case MQ_ERR_UNSUPPORTED: return "unsupported shape (needs K % 128 == 0, group 128, bk 64, bn 64 or 128, N % bn == 0)";
         case MQ_ERR_HIP: return "HIP runtime error";
+        case MQ_ERR_SCRATCH: return "shape needs more scratch than the library's static array (MQ_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -127,6 +153,21 @@ int mq_select_blocks(const float* w, const float* h, int64_t N, int64_t K, int g
                       (reinterpret_cast<uintptr_t>(workspace) & 7u)))
         return MQ_ERR_INVALID_ARG;
     return hip_status(mq::launch_select(w, h, N, K, bn, k_blocks, row_ptr, col_idx, delta, workspace,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int mq_select_blocks_noalloc(const float* w, const float* h, int64_t N, int64_t K, int group, int bn,
+                             int bk, int64_t k_blocks, int32_t* row_ptr, int32_t* col_idx, double* delta,
+                             void* stream) {
+    int rc = check_select(w, h, N, K, group, bn, bk, k_blocks, row_ptr, col_idx);
+    if (rc) return rc;
+    const int64_t nb = (N / bn) * (K / bk);
+    if (mq::select_scratch_bytes(nb, delta == nullptr) > MQ_NOALLOC_SCRATCH_BYTES) return MQ_ERR_SCRATCH;
+    void* buf = device_scratch();
+    if (!buf) return MQ_ERR_HIP;
+    // the kernels clear and fully rewrite the ranks and scores they use: nothing
+    // from an earlier call is read
+    return hip_status(mq::launch_select(w, h, N, K, bn, k_blocks, row_ptr, col_idx, delta, buf,
                                         static_cast<hipStream_t>(stream)));
 }
 

@@ -60,7 +60,8 @@ typedef enum {
     MQ_OK = 0,
     MQ_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned buffer, k_blocks > NB */
     MQ_ERR_UNSUPPORTED = -2,  /* shape outside the supported set above */
-    MQ_ERR_HIP = -3           /* a HIP runtime call or launch failed */
+    MQ_ERR_HIP = -3,          /* a HIP runtime call or launch failed */
+    MQ_ERR_SCRATCH = -4       /* the shape needs more than the library's static scratch */
 } mq_status;
 
 typedef enum { MQ_F32 = 0, MQ_BF16 = 1 } mq_dtype;
@@ -115,6 +116,26 @@ int mq_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* x
 int mq_select_blocks(const float* w, const float* h, int64_t N, int64_t K, int group, int bn,
                      int bk, int64_t k_blocks, int32_t* row_ptr, int32_t* col_idx,
                      double* delta, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mq_select_blocks for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, results and errors as mq_select_blocks without a workspace; its
+ * scratch (select ranks, and the scores when delta is NULL) is a static device
+ * array of MQ_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends. The call makes no allocation of any kind.
+ * Limit: 4 * NB bytes (rounded up to 8) plus 8 * NB when delta is NULL must fit,
+ * i.e. NB <= 349525 with delta NULL, NB <= 1048576 otherwise; larger shapes
+ * return MQ_ERR_SCRATCH with nothing launched. Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (different streams, or threads
+ * without ordering) race and give wrong results; order them on one stream.
+ * The first call on a device looks up the array's address on that device
+ * (hipGetSymbolAddress) with the device current.
+ */
+#define MQ_NOALLOC_SCRATCH_BYTES (4u << 20)
+int mq_select_blocks_noalloc(const float* w, const float* h, int64_t N, int64_t K, int group,
+                             int bn, int bk, int64_t k_blocks, int32_t* row_ptr,
+                             int32_t* col_idx, double* delta, void* stream);
 
 /* Workspace bytes mq_select_blocks needs for this shape with delta == NULL (12 * NB;
    4 * NB suffice when delta is given); 0 for an unsupported shape. */

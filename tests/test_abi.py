@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(mq):
         assert hasattr(lib, fn), fn
     assert set(_declared()) == set(mq.EXPORTS)
     assert mq.version() == 10100
-    for s in (0, -1, -2, -3):
+    for s in (0, -1, -2, -3, -4):
         assert mq.status_string(s)
 
 
@@ -115,6 +115,14 @@ def test_preparation_calls_reject_bad_arguments(lib_nogpu):
     assert lib.mq_gemm_w4a4_dense(FAKE, FAKE, FAKE, FAKE, 4, 512, 320, 128, FAKE, 0, None, None) == -2
     assert lib.mq_gemm_residual_separate(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 4, 512, 512,
                                          128, 64, 64, FAKE, 0, None, None) == -1
+    # the no-allocation selection refuses a shape whose ranks (and scores, with no
+    # delta output) exceed its static scratch, before touching the device
+    assert lib.mq_select_blocks_noalloc(FAKE, FAKE, 65536, 65536, 128, 64, 64, 5, FAKE, FAKE, None,
+                                        None) == -4
+    assert lib.mq_select_blocks_noalloc(FAKE, FAKE, 65536 + 64, 65536, 128, 64, 64, 5, FAKE, FAKE,
+                                        FAKE, None) == -4
+    assert lib.mq_select_blocks_noalloc(FAKE, FAKE, 512, 512, 128, 64, 64, nb + 1, FAKE, FAKE, FAKE,
+                                        None) == -1
     # the packed activation layout is group-major, so K must be a multiple of 128
     assert lib.mq_quantize_act(FAKE, 1, 4, 130, FAKE, FAKE, None) == -2
 
