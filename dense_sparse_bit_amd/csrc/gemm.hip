@@ -151,7 +151,7 @@ __device__ __forceinline__ void dec_compute(const DecStep<MT, QS>& st, const Gem
             // the base products of both row tiles first, then the residual MFMAs
             // accumulating onto 14 P (T = 14 P + Pr, exact): the base and the
             // residual operands are never live together
-            const float fr = (sc / 14.0f) * kF8Unit;
+            const float fr = div14(sc) * kF8Unit;
             v4f tv[MT];
             {
                 const v8i b = f8_operand(st.w[u]);
@@ -274,40 +274,68 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
 
 // ===========================================================================
 // Prefill kernel, M > 32: 128 x 128 output tile per workgroup, four waves of
-// 64 x 64, one K group (one fp8 MFMA deep) per step, two LDS stages.
-//   * Operand tiles move from memory to LDS without passing through registers
-//     (global_load_lds, 16 bytes per lane): each 16-row subtile of a group is one
-//     1 KB load, placed in LDS in MFMA lane order (lane 16 kc + r holds row r,
-//     codes 32 kc .. 32 kc + 31). The packed weight tiles already have that
-//     order; activation rows are gathered into it. No staging registers, no LDS
-//     store instructions, half the LDS bytes of fp8 operands, and every LDS read
-//     is one conflict-free 1 KB access.
-//   * Each wave widens its operands to fp8 after its LDS read (three operations
-//     per 8 codes) and dequantizes each group's exact products with the
-//     column's factor s * 2^18 (or fp32(s / 14) * 2^18 in a residual group).
-//   * Residual blocks: a wave's 64 columns lie in one block row, so whether a
-//     group holds a chosen block is the same for the whole wave (a scalar
-//     branch). Such a group takes a second MFMA per subtile on the residual
-//     codes, which the wave loads from memory one group ahead (zero for a
-//     half-group without a chosen block); the MFMA accumulates them onto 14 P,
-//     giving T = 14 P + Pr exactly, before the dequant.
-//   * The loads of group g+1 are issued right after group g's LDS reads and
-//     complete during its MFMAs: one wait and one barrier per group.
+// 64 x 64 (2 x 2), one 128-wide K group per step, 32 x 32 x 64 fp8 MFMAs.
+//   * The instruction is 64 inputs deep, so a group is two MFMAs per 32 x 32
+//     tile, one per half, and a chosen 64-wide residual block (one half of a
+//     group) is exactly one more MFMA per tile: no zero-padded depth.
+//   * Activations are widened once per workgroup: every wave loads 1 KB runs
+//     of the group's activation nibbles (16 rows x 64 bytes, lane 16 kc + r
+//     holds row r, bytes 16 kc .. 16 kc + 15), turns them into fp8 operand
+//     bytes and stores them in LDS in MFMA lane order, so each operand read is
+//     two conflict-free 1 KB LDS reads shared by the two waves of its rows.
+//   * Weights go straight from memory into registers (each wave owns its 64
+//     columns; the other wave that uses them finds them in L2), one group
+//     ahead, and are widened per wave right before their MFMAs.
+//   * Per group: exact products P (and Pr) of each 32 x 32 tile, then
+//     acc += fp32(s) * 2^18 * P, and acc += fp32(s / 14) * 2^18 * Pr for a
+//     half holding a chosen block of the wave's block row (a scalar branch:
+//     a wave's 64 columns lie in one block row).
+//   * One barrier per group: the next group's activations are written to the
+//     other LDS stage after this group's MFMAs; global loads are waited on by
+//     count (their registers are not read until a group later).
+// 32 x 32 MFMA layouts: operand lane l holds row (A) / column (B) l % 32 and
+// the inputs of K half l / 32; result register r of lane l is row
+// 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
 // ===========================================================================
 constexpr int kPM = 128, kPN = 128;
-typedef __attribute__((address_space(3))) void lds_void_t;
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ v16f mfma32_f8(v8i a, v8i b, v16f c) {
+    // format selectors 0/0 (e4m3 both operands), no block scales
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// One prefill step's register-resident loads (a group ahead of its use).
+struct PfLoads {
+    uint4 b[2][2];     // weight nibbles [column tile j][half h]
+    uint4 x[2];        // activation nibbles for the LDS fill (two 1 KB runs per wave)
+};
+
+// A group's residual codes of its first chosen half [column tile j] (zero where no
+// block is chosen); when both halves hold chosen blocks (rare at these budgets),
+// the second half's codes are fetched where they are used.
+struct PfRes {
+    uint4 r[2];
+    int rmask;         // bit h: half h of the group holds a chosen block (wave-uniform)
+    int jb1;           // CSR position of half 1's block, or -1
+};
 
 template <bool RES, bool DUMP, int OUTMODE>
 __global__ __launch_bounds__(256, DUMP ? 1 : 2) void k_gemm_prefill(GemmArgs a) {
-    __shared__ __align__(16) uint8_t tiles[2][2][8][1024];          // [stage][A, B][subtile][lane * 16]
+    // activation operands in fp8: two stages of two groups each,
+    // [stage][group slot][M tile 4][half 2][part 2][lane 64][16 B]
+    __shared__ __align__(16) uint8_t xs[2][2][4][2][2][1024];
     __shared__ int tab[RES ? 2 * 2 * kMaxGroups : 1];                // [2 block rows][2G]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int li = lane & 15, kg = lane >> 4;
+    // the wave index is uniform in a wave: say so, so that per-wave buffer
+    // resources live in scalar registers (no per-lane waterfall around each load)
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lc = lane & 31, lh = lane >> 5;
     const int wm = wave >> 1, wn = wave & 1;
     const int tiles_n = (a.N + kPN - 1) / kPN;
     const int m0 = (blockIdx.x / tiles_n) * kPM, n0 = (blockIdx.x % tiles_n) * kPN;
     const int G = a.K / kGroup, G4 = (G + 3) / 4, nbc = 2 * G;
     const int br0 = n0 / a.bn;
+    const int wc0 = n0 + wn * 64;                                    // this wave's first column
 
     // zipper tables of the tile's block rows (one or two), gathered once
     if (RES) {
@@ -318,167 +346,271 @@ __global__ __launch_bounds__(256, DUMP ? 1 : 2) void k_gemm_prefill(GemmArgs a) 
         __syncthreads();
     }
 
-    // Loads go through buffer resources with a per-group base: 32-bit lane offsets
-    // stay small, and rows past M or subtiles past N fall outside the range and
-    // read zero (their outputs are never stored). Wave w loads subtiles 2w and
-    // 2w+1 of both operands.
-    const int nsub = min(a.N / 16 - n0 / 16, 8);                    // column subtiles of this tile
-    const uint32_t a_range = static_cast<uint32_t>(min(a.M - m0, kPM)) * 64u;
-    const uint32_t b_range = static_cast<uint32_t>(nsub - 1) * static_cast<uint32_t>(G) * 1024u + 1024u;
-    uint32_t aoff[2], boff[2];
+    // weights of this wave's 64 columns: four 16-row tiles; tiles past N read zero
+    const int wtiles = max(0, min(4, (a.N - wc0) / 16));
+    const __amdgpu_buffer_rsrc_t rb =
+        buf_rsrc_uniform(a.wq + static_cast<int64_t>(wc0 >> 4) * G * 1024, static_cast<uint32_t>(wtiles) * G * 1024u);
+    // lane's offset for column tile j, half h (group 0): tile 2j + lc/16, row lc%16, chunk 2h + lh
+    uint32_t boff[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            boff[j][h] = static_cast<uint32_t>(2 * j + (lc >> 4)) * G * 1024u +
+                         static_cast<uint32_t>(((2 * h + lh) * 16 + (lc & 15)) * 16);
+    // the lane's column scales, four groups per 8-byte load (per column tile j)
+    const __amdgpu_buffer_rsrc_t rs =
+        buf_rsrc_uniform(a.sw + static_cast<int64_t>(wc0 >> 4) * G4 * 64, static_cast<uint32_t>(wtiles) * G4 * 128u);
+    uint32_t soff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        soff[j] = (static_cast<uint32_t>(2 * j + (lc >> 4)) * G4 * 64u + (lc & 15) * 4u) * 2u;
+
+    // residual payload of this wave's block row, and the lane's rows in it
+    __amdgpu_buffer_rsrc_t rr = buf_rsrc_uniform(a.wq, 0u);
+    int wtab = 0, wlo = 0;
+    uint32_t rrow = 0;
+    if (RES && wc0 < a.N) {
+        const int brw = wc0 / a.bn;
+        wtab = (brw - br0) * nbc;
+        wlo = clampi(a.row_ptr[brw], 0, a.nnz);
+        const int whi = clampi(a.row_ptr[brw + 1], wlo, a.nnz);
+        rr = buf_rsrc_uniform(whi > wlo ? a.rq + static_cast<int64_t>(wlo) * a.bn * 32 : a.wq,
+                      static_cast<uint32_t>(whi - wlo) * static_cast<uint32_t>(a.bn) * 32u);
+        rrow = static_cast<uint32_t>(wc0 % a.bn + lc);
+    }
+
+    // activation fill: this wave's two 1 KB runs of a group (rows 32 wave + 16 u + lane % 16)
+    const uint32_t x_range = static_cast<uint32_t>(max(0, min(a.M - m0, kPM))) * 64u;
+    uint32_t xoff[2];
+    int xdst[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int st = 2 * wave + u;
-        aoff[u] = static_cast<uint32_t>(16 * st + li) * 64u + kg * 16u;
-        boff[u] = static_cast<uint32_t>(st) * static_cast<uint32_t>(G) * 1024u + lane * 16u;
+        const int row = 32 * wave + 16 * u + (lane & 15), kc = lane >> 4;
+        xoff[u] = static_cast<uint32_t>(row) * 64u + kc * 16u;
+        const int lp = (row & 31) + 32 * (kc & 1);
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+            xdst[u][p] = ((((row >> 5) * 2 + (kc >> 1)) * 2 + p) * 64 + lp) * 16;
     }
-    auto issue = [&](int g, int stage) {
-        const __amdgpu_buffer_rsrc_t ra = buf_rsrc(a.xq + (static_cast<int64_t>(g) * a.M + m0) * 64, a_range);
-        const __amdgpu_buffer_rsrc_t rb = buf_rsrc(a.wq + wq_tile(n0 >> 4, G, g), b_range);
+
+    // Loads of the steady state are issued unconditionally (a group index past the
+    // end is clamped to the last group, an absent residual half reads past its
+    // buffer's range and returns zeros), so the compiler counts outstanding loads
+    // exactly and waits only for the data it uses.
+    auto load_x = [&](int g, PfLoads& L) {
+        const int gc = min(g, G - 1);
+        const __amdgpu_buffer_rsrc_t rx = buf_rsrc_uniform(a.xq + (static_cast<int64_t>(gc) * a.M + m0) * 64, x_range);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) L.x[u] = buf_load16(rx, xoff[u]);
+    };
+    auto load_w = [&](int g, PfLoads& L) {
+        const uint32_t gc = static_cast<uint32_t>(min(g, G - 1));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) L.b[j][h] = buf_load16(rb, boff[j][h] + gc * 1024u);
+    };
+    // the group's residual codes, fetched at the start of the step that uses them
+    // (before the next group's weights, so waiting for them does not wait for those)
+    auto res_off = [&](int jb, int j) {
+        return jb >= 0 ? ((jb - wlo) * static_cast<uint32_t>(a.bn) + rrow + 32u * j) * 32u + lh * 16u : 0x80000000u;
+    };
+    auto load_res = [&](int g, PfRes& R) {
+        const int jb0 = __builtin_amdgcn_readfirstlane(tab[wtab + 2 * g]);
+        const int jb1 = __builtin_amdgcn_readfirstlane(tab[wtab + 2 * g + 1]);
+        R.rmask = (jb0 >= 0 ? 1 : 0) | (jb1 >= 0 ? 2 : 0);
+        R.jb1 = jb1;
+        const int jb = jb0 >= 0 ? jb0 : jb1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) R.r[j] = buf_load16(rr, res_off(jb, j));
+    };
+    // widen the loaded activation runs into stage st of the LDS operands
+    auto store_x = [&](const PfLoads& L, int st, int slot) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int st = 2 * wave + u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)&tiles[stage][0][st][0], 16, aoff[u], 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)&tiles[stage][1][st][0], 16, boff[u], 0, 0, 0);
+            const v8i v = f8_operand(L.x[u]);
+            *reinterpret_cast<v4i*>(&xs[st][slot][0][0][0][0] + xdst[u][0]) = v4i{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<v4i*>(&xs[st][slot][0][0][0][0] + xdst[u][1]) = v4i{v[4], v[5], v[6], v[7]};
         }
     };
-    // the lane's four column scales of group g: one 16-bit load each
-    const __amdgpu_buffer_rsrc_t rs =
-        buf_rsrc(a.sw + static_cast<int64_t>(n0 >> 4) * G4 * 64, static_cast<uint32_t>(nsub) * static_cast<uint32_t>(G4) * 128u);
-    const uint32_t soff = (static_cast<uint32_t>(wn * 4) * static_cast<uint32_t>(G4) * 64u + li * 4u) * 2u;
-    auto scales = [&](int g, uint16_t (&sc)[4]) {
-        const int gs = ((g >> 2) * 64 + (g & 3)) * 2;
+    // the lane's fp16 scales of the current and the next quad of groups, per column tile
+    uint2 sc[2], scn[2];
+    auto load_scales = [&](int q, uint2 (&dst)[2]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            sc[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff + static_cast<uint32_t>(j) * static_cast<uint32_t>(G4) * 128u, gs, 0);
+        for (int j = 0; j < 2; ++j) dst[j] = buf_load8(rs, soff[j] + static_cast<uint32_t>(q) * 128u);
     };
 
-    // this wave's residual payload: its 64 columns' block row, as a buffer range
-    // (offsets past it read zero), and the lane's row in it for column subtile j
-    __amdgpu_buffer_rsrc_t rsrc = buf_rsrc(a.wq, 0u);
-    int wtab = 0, wlo = 0;
-    uint32_t rrow0 = 0;
-    if (RES) {
-        const int wc0 = n0 + wn * 64;
-        if (wc0 < a.N) {
-            const int brw = wc0 / a.bn;
-            wtab = (brw - br0) * nbc;
-            wlo = clampi(a.row_ptr[brw], 0, a.nnz);
-            const int whi = clampi(a.row_ptr[brw + 1], wlo, a.nnz);
-            rsrc = buf_rsrc(whi > wlo ? a.rq + static_cast<int64_t>(wlo) * a.bn * 32 : a.wq,
-                            static_cast<uint32_t>(whi - wlo) * static_cast<uint32_t>(a.bn) * 32u);
-        }
-        rrow0 = static_cast<uint32_t>((wc0 + li) % a.bn);
-    }
-    // residual codes of group g for this wave's columns; returns whether the wave
-    // has a chosen block in the group (the same in every lane)
-    auto fetch_res = [&](int g, uint4 (&rr)[4]) -> bool {
-        const int j0 = __builtin_amdgcn_readfirstlane(tab[wtab + 2 * g]);
-        const int j1 = __builtin_amdgcn_readfirstlane(tab[wtab + 2 * g + 1]);
-        if (j0 < 0 && j1 < 0) return false;
-        const int jb = kg < 2 ? j0 : j1;
+
+    v16f acc[2][2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t off = jb >= 0 ? ((jb - wlo) * static_cast<uint32_t>(a.bn) + rrow0 + 16 * j) * 32u + (kg & 1) * 16u
-                                         : 0xFFFFFFF0u;
-            rr[j] = buf_load16(rsrc, off);
-        }
-        return true;
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // debug build: the exact group sums, 14 P from the base pass, plus Pr from the
+    // residual pass (each entry is owned by one lane, so the update needs no atomics)
+    auto dump_idx = [&](int i, int j, int r, int g) -> int64_t {
+        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int nn = wc0 + j * 32 + lc;
+        return (m < a.M && nn < a.N) ? (static_cast<int64_t>(m) * a.N + nn) * G + g : -1;
+    };
+    auto a_operand = [&](int st, int i, int h) {
+        const uint8_t* base = &xs[st >> 1][st & 1][wm * 2 + i][h][0][0];
+        const v4i lo = *reinterpret_cast<const v4i*>(base + lane * 16);
+        const v4i hi = *reinterpret_cast<const v4i*>(base + 1024 + lane * 16);
+        return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
 
-    float acc[4][4][4];
+    // one group g (u = g % 4, a constant at every call site, so the scale word and
+    // half are picked without an index): operands of stage st, weights of L,
+    // residual codes of R, scales sc
+    auto compute = [&](int g, int u, int st, const PfLoads& L, const PfRes& R) {
+        float sv[2], fs[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
-    auto dump = [&](int g, int i, int j, int r, int T) {
-        const int m = m0 + wm * 64 + i * 16 + kg * 4 + r;
-        const int nn = n0 + wn * 64 + j * 16 + li;
-        if (m < a.M && nn < a.N) a.acc_dump[(static_cast<int64_t>(m) * a.N + nn) * G + g] = T;
-    };
-
-    uint16_t sc[4];
-    uint4 rr[4];
-    bool res_cur = false;
-    issue(0, 0);
-    scales(0, sc);
-    if (RES) res_cur = fetch_res(0, rr);
-    __builtin_amdgcn_s_waitcnt(0);   // all counters: the direct loads are not tracked by the barrier's fence
-    __syncthreads();
-    for (int g = 0; g < G; ++g) {
-        const int stage = g & 1;
-        uint4 araw[4], braw[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) araw[i] = *reinterpret_cast<const uint4*>(&tiles[stage][0][wm * 4 + i][lane * 16]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) braw[j] = *reinterpret_cast<const uint4*>(&tiles[stage][1][wn * 4 + j][lane * 16]);
-        const bool res = RES && res_cur;
-        float f[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float s = f16_bits_to_f32(sc[j]);
-            f[j] = res ? (s / 14.0f) * kF8Unit : s * kF8Unit;
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t w2 = (u & 2) ? sc[j].y : sc[j].x;
+            sv[j] = f16_bits_to_f32(static_cast<uint16_t>(w2 >> (16 * (u & 1))));
+            fs[j] = sv[j] * kF8Unit;
         }
-        // the next group's loads (the last step re-loads group G-1 into the idle stage)
-        const int gn = min(g + 1, G - 1);
-        issue(gn, stage ^ 1);
-        scales(gn, sc);
-        // next group's residual codes: now if this group does not use the
-        // registers, else after its residual MFMAs
-        bool res_next = false;
-        if (RES && !res && g + 1 < G) res_next = fetch_res(g + 1, rr);
-        v8i av[4], bv[4];
+        // base pass: every group, acc += s * P
+        v8i bop[2][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) av[i] = f8_operand(araw[i]);
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bv[j] = f8_operand(braw[j]);
-        if (res) {
+            for (int h = 0; h < 2; ++h) bop[j][h] = f8_operand(L.b[j][h]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const v8i rv = f8_operand(rr[j]);
+        for (int i = 0; i < 2; ++i) {
+            const v8i a0 = a_operand(st, i, 0), a1 = a_operand(st, i, 1);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const v4f p = mfma_f8(av[i], bv[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-                    // T = 14 P + Pr: the residual MFMA accumulates onto 14 P (exact:
-                    // every partial sum is a multiple of 2^-18 far below 2^6)
-                    const v4f t = mfma_f8(av[i], rv, p * 14.0f);
+            for (int j = 0; j < 2; ++j) {
+                const v16f z = {};
+                v16f p = mfma32_f8(a0, bop[j][0], z);
+                p = mfma32_f8(a1, bop[j][1], p);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        acc[i][j][r] = fmaf(f[j], t[r], acc[i][j][r]);
-                        if (DUMP) dump(g, i, j, r, static_cast<int>(t[r] * kF8Unit));
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(fs[j], p[r], acc[i][j][r]);
+                if (DUMP) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int64_t d = dump_idx(i, j, r, g);
+                        if (d >= 0) a.acc_dump[d] = 14 * static_cast<int>(p[r] * kF8Unit);
                     }
                 }
             }
-        } else {
+        }
+        // residual pass, only in a group whose half (or halves) hold a chosen block
+        // of the wave's block row (a scalar branch): one MFMA per tile and chosen
+        // half on the same LDS activation operands, acc += fp32(s / 14) * Pr
+        const int rmask = RES ? R.rmask : 0;
+        if (RES && rmask) {
+            const int ha = (rmask & 1) ? 0 : 1;         // the half whose codes R holds
+            const bool both = rmask == 3;
+            float fr[2];
+            v8i ra[2], rb2[2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j) {
+                fr[j] = div14(sv[j]) * kF8Unit;
+                ra[j] = f8_operand(R.r[j]);
+            }
+            if (both) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const v4f p = mfma_f8(av[i], bv[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+                for (int j = 0; j < 2; ++j) rb2[j] = f8_operand(buf_load16(rr, res_off(R.jb1, j)));
+            }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        acc[i][j][r] = fmaf(f[j], p[r], acc[i][j][r]);
-                        if (DUMP) dump(g, i, j, r, 14 * static_cast<int>(p[r] * kF8Unit));
+            for (int i = 0; i < 2; ++i) {
+                const v8i aa = a_operand(st, i, ha);
+                v8i ab;
+                if (both) ab = a_operand(st, i, 1);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const v16f z = {};
+                    v16f pr = mfma32_f8(aa, ra[j], z);
+                    if (both) pr = mfma32_f8(ab, rb2[j], pr);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(fr[j], pr[r], acc[i][j][r]);
+                    if (DUMP) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int64_t d = dump_idx(i, j, r, g);
+                            if (d >= 0) a.acc_dump[d] += static_cast<int>(pr[r] * kF8Unit);
+                        }
                     }
                 }
+            }
         }
-        if (RES && res && g + 1 < G) res_next = fetch_res(g + 1, rr);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        res_cur = res_next;
+    };
+
+    // Pipeline: a stage of LDS holds the activation operands of two consecutive
+    // groups, so one barrier serves two groups. Step g computes group g from
+    // stage (g/2)%2, slot g%2, with its weights in Lc; it stores group g+2's
+    // activations (loaded a step earlier, in Lc.x) into the other stage, and loads
+    // group g+1's weights and group g+3's activations into Ln. The loop is
+    // unrolled by a quad of groups, so the two register sets alternate without
+    // copies and u = g % 4 is a constant.
+    PfLoads L0, L1;
+    load_x(0, L0);
+    load_w(0, L0);
+    load_scales(0, sc);
+    load_scales(min(1, G4 - 1), scn);
+    store_x(L0, 0, 0);
+    load_x(1, L0);
+    store_x(L0, 0, 1);
+    load_x(2, L0);
+    __syncthreads();
+    auto step = [&](int g, int u, PfLoads& Lc, PfLoads& Ln) {
+        PfRes R;
+        R.rmask = 0;
+        if (RES) load_res(g, R);
+        load_w(g + 1, Ln);
+        if (u == 0 && g > 0) {
+            // the prefetched scales become current; the next quad's are loaded
+#pragma unroll
+            for (int j = 0; j < 2; ++j) sc[j] = scn[j];
+            load_scales(min((g >> 2) + 1, G4 - 1), scn);
+        }
+        compute(g, u, ((u >> 1) << 1) | (u & 1), Lc, R);
+        store_x(Lc, ((u >> 1) & 1) ^ 1, u & 1);
+        load_x(g + 3, Ln);
+        if (u & 1) __syncthreads();
+    };
+    for (int g = 0; g < G; g += 4) {
+        step(g, 0, L0, L1);
+        if (g + 1 >= G) break;
+        step(g + 1, 1, L1, L0);
+        if (g + 2 >= G) break;
+        step(g + 2, 2, L0, L1);
+        if (g + 3 >= G) break;
+        step(g + 3, 3, L1, L0);
     }
 
+    // Epilogue: the lane's 32 token scales are loaded together (rows past M read
+    // zero through the range check), then y = acc * sx is stored as bf16 or fp32.
+    const int mw = m0 + wm * 64;
+    float sxr[2][16];
+    if (OUTMODE == 0) {
+        const __amdgpu_buffer_rsrc_t rsx = buf_rsrc_uniform(a.sx + mw, static_cast<uint32_t>(max(0, min(64, a.M - mw))) * 4u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int nn = n0 + wn * 64 + j * 16 + li;
+            for (int r = 0; r < 16; ++r)
+                sxr[i][r] = __builtin_bit_cast(float, buf_load4(rsx, static_cast<uint32_t>(i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)) * 4u));
+    }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * 64 + i * 16 + kg * 4 + r;
-                if (m < a.M && nn < a.N) store_out(a, OUTMODE, m, nn, acc[i][j][r]);
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int nn = wc0 + j * 32 + lc;
+            if (nn >= a.N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = mw + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (m >= a.M) continue;
+                const int64_t idx = static_cast<int64_t>(m) * a.N + nn;
+                if (OUTMODE == 1) a.ws[idx] = acc[i][j][r];
+                else if (a.y_bf16) static_cast<uint16_t*>(a.y)[idx] = f32_to_bf16_bits(acc[i][j][r] * sxr[i][r]);
+                else static_cast<float*>(a.y)[idx] = acc[i][j][r] * sxr[i][r];
             }
         }
 }
@@ -513,7 +645,7 @@ __global__ __launch_bounds__(256) void k_residual_merge(GemmArgs a) {
             const v8i aop = v8i{(int)f8_even(av.x), (int)f8_odd(av.x), (int)f8_even(av.y), (int)f8_odd(av.y), 0, 0, 0, 0};
             const v8i bop = v8i{(int)f8_even(rv.x), (int)f8_odd(rv.x), (int)f8_even(rv.y), (int)f8_odd(rv.y), 0, 0, 0, 0};
             const v4f c = mfma_f8(aop, bop, v4f{0.0f, 0.0f, 0.0f, 0.0f});
-            const float sr = f16_bits_to_f32(a.sw[sw_index(n, G4, g)]) / 14.0f;
+            const float sr = div14(f16_bits_to_f32(a.sw[sw_index(n, G4, g)]));
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = fmaf(sr * kF8Unit, c[r], acc[r]);
         }

@@ -69,6 +69,17 @@ __device__ __forceinline__ float rtn_codef(float v, float s, float rs) {
     return fminf(fmaxf(rint_quot(v, s, rs), -7.0f), 7.0f);
 }
 
+// fp32(s / 14) for an fp16 scale s without a division: a product by fl(1/14)
+// and one fma correction. For every finite binary16 value s this equals the
+// correctly rounded quotient (checked exhaustively on the host by the test suite),
+// so the GEMM's residual grid is the same s_r = fp32(s / 14) as the packing's.
+__device__ __forceinline__ float div14(float s) {
+    constexpr float c = 1.0f / 14.0f;
+    const float q = s * c;
+    const float r = __builtin_fmaf(-q, 14.0f, s);
+    return __builtin_fmaf(r, c, q);
+}
+
 // Per-group constants of the decomposition W ~ s*q + s_r*r for an fp16 scale s.
 struct GroupScale {
     float s, rs, sr, rsr;   // s, 1/s, s_r = s/14, 1/s_r (all correctly rounded)
@@ -182,6 +193,15 @@ constexpr int kBufferFlags = 0x00020000;   // dword 3 of a raw (untyped) gfx9 bu
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                              static_cast<int>(bytes), kBufferFlags);
+}
+// The same resource from values the caller knows to be wave-uniform but the
+// compiler may not (it would otherwise wrap every load in a per-lane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc_uniform(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+    return buf_rsrc(reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo),
+                    __builtin_amdgcn_readfirstlane(bytes));
 }
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
