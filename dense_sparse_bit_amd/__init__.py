@@ -33,6 +33,10 @@ _p, _i64, _int = C.c_void_p, C.c_int64, C.c_int
 _SIGS = {
     "mq_hessian_diag": [_p, _int, _i64, _i64, _p, _p],
     "mq_quantize_act": [_p, _int, _i64, _i64, _p, _p, _p],
+    "mq_quantize_act_scaled": [_p, _int, _i64, _i64, _p, _p, _p, _p],
+    "mq_hessian_diag_scaled": [_p, _int, _i64, _i64, _p, _p, _p],
+    "mq_smooth_factors": [_p, _int, _i64, _i64, _p, _i64, _p, _p, _p],
+    "mq_scale_columns": [_p, _i64, _i64, _p, _p, _p],
     "mq_select_blocks": [_p, _p, _i64, _i64, _int, _int, _int, _i64, _p, _p, _p, _p, C.c_size_t, _p],
     "mq_select_blocks_noalloc": [_p, _p, _i64, _i64, _int, _int, _int, _i64, _p, _p, _p, _p],
     "mq_pack_weights": [_p, _i64, _i64, _int, _int, _int, _p, _p, _i64, _p, _p, _p, _p],
@@ -144,20 +148,28 @@ def _shape2(t, name):
 
 
 # --------------------------------------------------------------------------- a0
-def hessian_diag(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+def hessian_diag(x: torch.Tensor, out: torch.Tensor | None = None, r: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """h = mean over tokens of x^2 per channel (of x * r when r is given)."""
     M, K = _shape2(x, "x")
     _x_dtype(x)
     _device_contig(x, "x")
     h = torch.empty(K, dtype=torch.float32, device=x.device) if out is None else _buf(out, "h", 4 * K, _F32)
-    _on_device(x=x, h=h)
-    _call("mq_hessian_diag", _ptr(x), _x_dtype(x), M, K, _ptr(h), _stream(stream))
+    if r is not None:
+        _buf(r, "r", 4 * K, _F32)
+    _on_device(x=x, h=h, r=r)
+    if r is None:
+        _call("mq_hessian_diag", _ptr(x), _x_dtype(x), M, K, _ptr(h), _stream(stream))
+    else:
+        _call("mq_hessian_diag_scaled", _ptr(x), _x_dtype(x), M, K, _ptr(r), _ptr(h), _stream(stream))
     return h
 
 
 # --------------------------------------------------------------------------- a4
 def quantize_act(x: torch.Tensor, xq: torch.Tensor | None = None, sx: torch.Tensor | None = None,
-                 stream=None):
-    """Returns (xq u8 [K/128][M][64], sx fp32 [M])."""
+                 r: torch.Tensor | None = None, stream=None):
+    """Returns (xq u8 [K/128][M][64], sx fp32 [M]). With r (fp32 [K], from
+    smooth_factors) the migrated activations x * r are quantized."""
     M, K = _shape2(x, "x")
     _x_dtype(x)
     _device_contig(x, "x")
@@ -169,9 +181,47 @@ def quantize_act(x: torch.Tensor, xq: torch.Tensor | None = None, sx: torch.Tens
         sx = torch.empty(M, dtype=torch.float32, device=x.device)
     else:
         _buf(sx, "sx", 4 * M, _F32)
-    _on_device(x=x, xq=xq, sx=sx)
-    _call("mq_quantize_act", _ptr(x), _x_dtype(x), M, K, _ptr(xq), _ptr(sx), _stream(stream))
+    if r is not None:
+        _buf(r, "r", 4 * K, _F32, 16)
+    _on_device(x=x, xq=xq, sx=sx, r=r)
+    if r is None:
+        _call("mq_quantize_act", _ptr(x), _x_dtype(x), M, K, _ptr(xq), _ptr(sx), _stream(stream))
+    else:
+        _call("mq_quantize_act_scaled", _ptr(x), _x_dtype(x), M, K, _ptr(r), _ptr(xq), _ptr(sx),
+              _stream(stream))
     return xq, sx
+
+
+# --------------------------------------------------------------------------- a0' migration
+def smooth_factors(x: torch.Tensor, w: torch.Tensor, s=None, r=None, stream=None):
+    """Per-channel migration factors (s, r = 1/s), fp32 [K] each (alpha = 1/2)."""
+    M, K = _shape2(x, "x")
+    N, K2 = _shape2(w, "w")
+    if K2 != K:
+        raise ValueError(f"x has {K} channels, w has {K2}")
+    _x_dtype(x)
+    if w.dtype != torch.float32:
+        raise TypeError("w must be float32")
+    _device_contig(x, "x")
+    _device_contig(w, "w")
+    s = torch.empty(K, dtype=torch.float32, device=w.device) if s is None else _buf(s, "s", 4 * K, _F32)
+    r = torch.empty(K, dtype=torch.float32, device=w.device) if r is None else _buf(r, "r", 4 * K, _F32)
+    _on_device(x=x, w=w, s=s, r=r)
+    _call("mq_smooth_factors", _ptr(x), _x_dtype(x), M, K, _ptr(w), N, _ptr(s), _ptr(r), _stream(stream))
+    return s, r
+
+
+def scale_columns(w: torch.Tensor, s: torch.Tensor, out=None, stream=None):
+    """The migrated weights W diag(s), fp32 [N][K]."""
+    N, K = _shape2(w, "w")
+    if w.dtype != torch.float32:
+        raise TypeError("w must be float32")
+    _device_contig(w, "w")
+    _buf(s, "s", 4 * K, _F32, 16)
+    out = torch.empty_like(w) if out is None else _buf(out, "out", 4 * N * K, _F32, 16)
+    _on_device(w=w, s=s, out=out)
+    _call("mq_scale_columns", _ptr(w), N, K, _ptr(s), _ptr(out), _stream(stream))
+    return out
 
 
 # --------------------------------------------------------------------------- a2
@@ -371,13 +421,19 @@ def gemm_residual_separate(xq, sx, wq, sw, row_ptr, col_idx, rq, K: int, bn: int
     return y
 
 
-def forward_layer(x, w, k_blocks: int, bn: int = 64, out_dtype=torch.bfloat16, stream=None):
-    """The whole path on device: h -> select -> pack -> quantize X -> fused GEMM."""
-    h = hessian_diag(x, stream=stream)
+def forward_layer(x, w, k_blocks: int, bn: int = 64, out_dtype=torch.bfloat16, migrate: bool = False,
+                  stream=None):
+    """The whole path on device: (optional outlier migration) -> h -> select -> pack
+    -> quantize X -> fused GEMM."""
+    s = r = None
+    if migrate:
+        s, r = smooth_factors(x, w, stream=stream)
+        w = scale_columns(w, s, stream=stream)
+    h = hessian_diag(x, r=r, stream=stream)
     row_ptr, col_idx, delta = select_blocks(w, h, k_blocks, bn=bn, stream=stream)
     wq, sw, rq = pack_weights(w, row_ptr, col_idx, bn=bn, stream=stream)
-    xq, sx = quantize_act(x, stream=stream)
+    xq, sx = quantize_act(x, r=r, stream=stream)
     y = gemm_w4a4_residual(xq, sx, wq, sw, row_ptr, col_idx, rq, w.shape[1], bn=bn,
                            out_dtype=out_dtype, stream=stream)
     return dict(h=h, row_ptr=row_ptr, col_idx=col_idx, delta=delta, wq=wq, sw=sw, rq=rq, xq=xq,
-                sx=sx, y=y)
+                sx=sx, y=y, s=s, r=r, w_hat=w if migrate else None)

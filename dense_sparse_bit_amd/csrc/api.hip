@@ -131,7 +131,28 @@ int mq_version(void) { return kVersion; }
 int mq_hessian_diag(const void* x, int x_dtype, int64_t M, int64_t K, float* h, void* stream) {
     if (M <= 0 || K <= 0 || !x || !h || bad_dtype(x_dtype)) return MQ_ERR_INVALID_ARG;
     if (M * K > (int64_t(1) << 40)) return MQ_ERR_UNSUPPORTED;
-    return hip_status(mq::launch_hessian(x, x_dtype == MQ_BF16, M, K, h, static_cast<hipStream_t>(stream)));
+    return hip_status(mq::launch_hessian(x, x_dtype == MQ_BF16, M, K, nullptr, h, static_cast<hipStream_t>(stream)));
+}
+
+int mq_hessian_diag_scaled(const void* x, int x_dtype, int64_t M, int64_t K, const float* r, float* h,
+                           void* stream) {
+    if (M <= 0 || K <= 0 || !x || !h || !r || bad_dtype(x_dtype)) return MQ_ERR_INVALID_ARG;
+    if (M * K > (int64_t(1) << 40)) return MQ_ERR_UNSUPPORTED;
+    return hip_status(mq::launch_hessian(x, x_dtype == MQ_BF16, M, K, r, h, static_cast<hipStream_t>(stream)));
+}
+
+int mq_smooth_factors(const void* x, int x_dtype, int64_t M, int64_t K, const float* w, int64_t N, float* s,
+                      float* r, void* stream) {
+    if (M <= 0 || K <= 0 || N <= 0 || !x || !w || !s || !r || bad_dtype(x_dtype)) return MQ_ERR_INVALID_ARG;
+    if (M * K > (int64_t(1) << 40) || N * K > (int64_t(1) << 40)) return MQ_ERR_UNSUPPORTED;
+    return hip_status(mq::launch_smooth(x, x_dtype == MQ_BF16, M, K, w, N, s, r, static_cast<hipStream_t>(stream)));
+}
+
+int mq_scale_columns(const float* w, int64_t N, int64_t K, const float* s, float* w_hat, void* stream) {
+    if (N <= 0 || K <= 0 || (K & 3) || !w || !s || !w_hat) return MQ_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(s) || !aligned16(w_hat)) return MQ_ERR_INVALID_ARG;
+    if (N * K > (int64_t(1) << 40)) return MQ_ERR_UNSUPPORTED;
+    return hip_status(mq::launch_scale_cols(w, N, K, s, w_hat, static_cast<hipStream_t>(stream)));
 }
 
 int mq_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* xq, float* sx,
@@ -140,7 +161,17 @@ int mq_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* x
     if (K % mq::kGroup || M > (int64_t(1) << 31) - 1 || M * K > (int64_t(1) << 40)) return MQ_ERR_UNSUPPORTED;
     if (M == 0) return MQ_OK;
     if (!x || !xq || !sx || !aligned16(x) || !aligned16(xq)) return MQ_ERR_INVALID_ARG;
-    return hip_status(mq::launch_quant_act(x, x_dtype == MQ_BF16, M, K, xq, sx, static_cast<hipStream_t>(stream)));
+    return hip_status(mq::launch_quant_act(x, x_dtype == MQ_BF16, M, K, nullptr, xq, sx,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int mq_quantize_act_scaled(const void* x, int x_dtype, int64_t M, int64_t K, const float* r, uint8_t* xq,
+                           float* sx, void* stream) {
+    if (M < 0 || K <= 0 || (K & 1) || bad_dtype(x_dtype)) return MQ_ERR_INVALID_ARG;
+    if (K % mq::kGroup || M > (int64_t(1) << 31) - 1 || M * K > (int64_t(1) << 40)) return MQ_ERR_UNSUPPORTED;
+    if (M == 0) return MQ_OK;
+    if (!x || !xq || !sx || !r || !aligned16(x) || !aligned16(xq) || !aligned16(r)) return MQ_ERR_INVALID_ARG;
+    return hip_status(mq::launch_quant_act(x, x_dtype == MQ_BF16, M, K, r, xq, sx, static_cast<hipStream_t>(stream)));
 }
 
 int mq_select_blocks(const float* w, const float* h, int64_t N, int64_t K, int group, int bn, int bk,

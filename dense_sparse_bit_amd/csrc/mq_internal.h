@@ -36,9 +36,15 @@ inline size_t select_scratch_bytes(int64_t nb, bool scores) {
     return ranks + (scores ? static_cast<size_t>(nb) * 8 : 0);
 }
 
-hipError_t launch_hessian(const void* x, int bf16, int64_t M, int64_t K, float* h, hipStream_t st);
-hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, uint8_t* xq, float* sx,
-                            hipStream_t st);
+// colscale: per-channel multipliers r_k applied to x before the step (the migrated
+// activations x^ = fp32(x * r_k)), or null
+hipError_t launch_hessian(const void* x, int bf16, int64_t M, int64_t K, const float* colscale, float* h,
+                          hipStream_t st);
+hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, const float* colscale, uint8_t* xq,
+                            float* sx, hipStream_t st);
+hipError_t launch_smooth(const void* x, int bf16, int64_t M, int64_t K, const float* w, int64_t N, float* s,
+                         float* r, hipStream_t st);
+hipError_t launch_scale_cols(const float* in, int64_t rows, int64_t K, const float* c, float* out, hipStream_t st);
 // scratch: select_scratch_bytes(nb, delta == null) bytes, or null for a stream-ordered allocation
 hipError_t launch_select(const float* w, const float* h, int64_t N, int64_t K, int bn,
                          int64_t k_blocks, int32_t* row_ptr, int32_t* col_idx, double* delta,

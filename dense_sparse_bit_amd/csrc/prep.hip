@@ -33,7 +33,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kHCh = 64, kHRows = 128;
 
 __global__ __launch_bounds__(256) void k_hessian(const void* __restrict__ x, int bf16, int64_t M,
-                                                 int64_t K, float* __restrict__ h) {
+                                                 int64_t K, const float* __restrict__ colscale,
+                                                 float* __restrict__ h) {
     __shared__ float tile[kHRows][kHCh + 1];
     const int64_t k0 = static_cast<int64_t>(blockIdx.x) * kHCh;
     const int t = threadIdx.x;
@@ -45,6 +46,8 @@ __global__ __launch_bounds__(256) void k_hessian(const void* __restrict__ x, int
         for (int i = 0; i < kHRows * kHCh / 256; ++i) {
             const int idx = t + 256 * i, r = idx / kHCh, c = idx % kHCh;
             v[i] = (r < rows && k0 + c < K) ? load_x(x, bf16, (m0 + r) * K + k0 + c) : 0.0f;
+            // migrated activations x^ = fp32(x * r_k) (one rounding, as the definition)
+            if (colscale && k0 + c < K) v[i] = v[i] * colscale[k0 + c];
         }
         __syncthreads();
 #pragma unroll
@@ -71,7 +74,8 @@ __global__ __launch_bounds__(256) void k_hessian(const void* __restrict__ x, int
 // ---------------------------------------------------------------------------
 constexpr int kQaWords = 4;     // words kept in registers per thread (K <= 8192 read once)
 
-__device__ __forceinline__ void load8(const void* row, bool bf16, int64_t j, float (&v)[8]) {
+__device__ __forceinline__ void load8(const void* row, bool bf16, int64_t j, float (&v)[8],
+                                      const float* __restrict__ colscale) {
     if (bf16) {
         const uint4 u = static_cast<const uint4*>(row)[j];
         const uint32_t p[4] = {u.x, u.y, u.z, u.w};
@@ -86,9 +90,17 @@ __device__ __forceinline__ void load8(const void* row, bool bf16, int64_t j, flo
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
         v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
+    // migrated activations: x^ = fp32(x * r_k), one rounding per element
+    if (colscale) {
+        const float4 a = reinterpret_cast<const float4*>(colscale)[2 * j];
+        const float4 b = reinterpret_cast<const float4*>(colscale)[2 * j + 1];
+        v[0] = v[0] * a.x; v[1] = v[1] * a.y; v[2] = v[2] * a.z; v[3] = v[3] * a.w;
+        v[4] = v[4] * b.x; v[5] = v[5] * b.y; v[6] = v[6] * b.z; v[7] = v[7] * b.w;
+    }
 }
 
 __global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, int bf16, int64_t M, int64_t K,
+                                                   const float* __restrict__ colscale,
                                                    uint8_t* __restrict__ xq, float* __restrict__ sx) {
     const int64_t m = blockIdx.x, W = K / 8;
     const void* row = bf16 ? static_cast<const void*>(static_cast<const uint16_t*>(x) + m * K)
@@ -102,7 +114,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, i
     for (int i = 0; i < kQaWords; ++i) {
         const int64_t j = t + 256 * i;
         if (j < W) {
-            load8(row, bf16, j, v[i]);
+            load8(row, bf16, j, v[i], colscale);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
@@ -112,7 +124,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, i
     }
     for (int64_t j = t + 256 * kQaWords; j < W; j += 256) {
         float u[8];
-        load8(row, bf16, j, u);
+        load8(row, bf16, j, u, colscale);
 #pragma unroll
         for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(u[e]));
     }
@@ -150,7 +162,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, i
             uint8_t c = 0;
             if (j < W) {
                 float u[8];
-                load8(row, bf16, j, u);
+                load8(row, bf16, j, u, colscale);
                 c = static_cast<uint8_t>(static_cast<int>(rtn_codef(u[l & 7], s, rs)) & 15);
             }
             fixb[t >> 6][l] = c;
@@ -173,7 +185,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, i
     }
     for (int64_t j = t + 256 * kQaWords; j < W; j += 256) {
         float u[8];
-        load8(row, bf16, j, u);
+        load8(row, bf16, j, u, colscale);
         uint32_t n8 = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) n8 |= (static_cast<uint32_t>(static_cast<int>(rtn_codef(u[e], s, rs))) & 15u) << (4 * e);
@@ -555,15 +567,72 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_hessian(const void* x, int bf16, int64_t M, int64_t K, float* h, hipStream_t st) {
+hipError_t launch_hessian(const void* x, int bf16, int64_t M, int64_t K, const float* colscale, float* h,
+                          hipStream_t st) {
     const int64_t blocks = (K + kHCh - 1) / kHCh;
-    k_hessian<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st>>>(x, bf16, M, K, h);
+    k_hessian<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st>>>(x, bf16, M, K, colscale, h);
     return hipGetLastError();
 }
 
-hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, uint8_t* xq, float* sx,
-                            hipStream_t st) {
-    k_quant_act<<<dim3(static_cast<unsigned>(M)), dim3(256), 0, st>>>(x, bf16, M, K, xq, sx);
+hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, const float* colscale, uint8_t* xq,
+                            float* sx, hipStream_t st) {
+    k_quant_act<<<dim3(static_cast<unsigned>(M)), dim3(256), 0, st>>>(x, bf16, M, K, colscale, xq, sx);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// a0' (offline): migration factors of the equivalent per-channel transform
+// (Methodology 1): s_k = sqrt(a_k) / sqrt(b_k) with a_k = max_m |x_mk|,
+// b_k = max_n |w_nk| (fp32, correctly rounded square roots and division),
+// s_k = 1 for a dead channel; r_k = 1 / s_k. A workgroup owns 64 channels; its
+// four row lanes take every fourth row of X and of W (max is exact in any order).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_smooth(const void* __restrict__ x, int bf16, int64_t M, int64_t K,
+                                                const float* __restrict__ w, int64_t N, float* __restrict__ s,
+                                                float* __restrict__ r) {
+    __shared__ float red[2][4][64];
+    const int t = threadIdx.x, c = t & 63, lane_row = t >> 6;
+    const int64_t k = static_cast<int64_t>(blockIdx.x) * 64 + c;
+    float a = 0.0f, b = 0.0f;
+    if (k < K) {
+        for (int64_t m = lane_row; m < M; m += 4) a = fmaxf(a, fabsf(load_x(x, bf16, m * K + k)));
+        for (int64_t n = lane_row; n < N; n += 4) b = fmaxf(b, fabsf(w[n * K + k]));
+    }
+    red[0][lane_row][c] = a;
+    red[1][lane_row][c] = b;
+    __syncthreads();
+    if (t < 64 && k < K) {
+        a = fmaxf(fmaxf(red[0][0][c], red[0][1][c]), fmaxf(red[0][2][c], red[0][3][c]));
+        b = fmaxf(fmaxf(red[1][0][c], red[1][1][c]), fmaxf(red[1][2][c], red[1][3][c]));
+        const float sk = (a > 0.0f && b > 0.0f) ? sqrtf(a) / sqrtf(b) : 1.0f;
+        s[k] = sk;
+        r[k] = 1.0f / sk;
+    }
+}
+
+// out[i][k] = fp32(in[i][k] * c[k]): the migrated weights W^ = W diag(s)
+__global__ __launch_bounds__(256) void k_scale_cols(const float* __restrict__ in, int64_t rows, int64_t K,
+                                                    const float* __restrict__ c, float* __restrict__ out) {
+    const int64_t n4 = rows * K / 4;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        const float4 v = reinterpret_cast<const float4*>(in)[i];
+        const int64_t k = (i * 4) % K;
+        const float4 f = *reinterpret_cast<const float4*>(c + k);
+        reinterpret_cast<float4*>(out)[i] = make_float4(v.x * f.x, v.y * f.y, v.z * f.z, v.w * f.w);
+    }
+}
+
+hipError_t launch_smooth(const void* x, int bf16, int64_t M, int64_t K, const float* w, int64_t N, float* s,
+                         float* r, hipStream_t st) {
+    k_smooth<<<dim3(static_cast<unsigned>((K + 63) / 64)), dim3(256), 0, st>>>(x, bf16, M, K, w, N, s, r);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_cols(const float* in, int64_t rows, int64_t K, const float* c, float* out, hipStream_t st) {
+    const int64_t n4 = rows * K / 4;
+    const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n4 + 255) / 256, 8192));
+    if (blocks) k_scale_cols<<<dim3(blocks), dim3(256), 0, st>>>(in, rows, K, c, out);
     return hipGetLastError();
 }
 

@@ -81,6 +81,34 @@ int mq_version(void);
 int mq_hessian_diag(const void* x, int x_dtype, int64_t M, int64_t K, float* h, void* stream);
 
 /*
+ * Migration of activation outliers into the weights by an equivalent per-channel
+ * transform (Methodology 1: the method starts by moving activation outliers into
+ * the weight matrix, SmoothQuant being one such transform; the exponent is not
+ * given, alpha = 1/2 here):
+ *   a_k = max_m |x[m][k]|, b_k = max_n |w[n][k]|,
+ *   s[k] = sqrtf(a_k) / sqrtf(b_k)  (fp32, correctly rounded), 1 when a_k or b_k is 0,
+ *   r[k] = 1 / s[k].
+ * The migrated layer is W^ = W diag(s) (mq_scale_columns) and X^ = X diag(r), which
+ * the *_scaled calls below apply on the fly: X^ W^T = X W^T up to rounding.
+ * x: [M][K] fp32 or bf16, w: fp32 [N][K], s and r: fp32 [K]. Asynchronous on `stream`.
+ */
+int mq_smooth_factors(const void* x, int x_dtype, int64_t M, int64_t K, const float* w, int64_t N,
+                      float* s, float* r, void* stream);
+
+/* w_hat[n][k] = fp32(w[n][k] * s[k]) (the migrated weights). K % 4 == 0; w, s and
+ * w_hat 16-byte aligned; w_hat may equal w (in place). */
+int mq_scale_columns(const float* w, int64_t N, int64_t K, const float* s, float* w_hat, void* stream);
+
+/* mq_hessian_diag of the migrated activations x^[m][k] = fp32(x[m][k] * r[k]). */
+int mq_hessian_diag_scaled(const void* x, int x_dtype, int64_t M, int64_t K, const float* r, float* h,
+                           void* stream);
+
+/* mq_quantize_act of the migrated activations x^[m][k] = fp32(x[m][k] * r[k]); the
+ * per-call path of a migrated layer (r 16-byte aligned). */
+int mq_quantize_act_scaled(const void* x, int x_dtype, int64_t M, int64_t K, const float* r, uint8_t* xq,
+                           float* sx, void* stream);
+
+/*
  * Per-token symmetric int4 activation quantization (the W4A4 setting of the
  * Experimental Results; "quantization" is the first stage of the ZipperEngine
  * pipeline, Methodology 3).

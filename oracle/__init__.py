@@ -63,9 +63,11 @@ def load(path: str = LIB):
     lib.or_output.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p]
     lib.or_distortion.argtypes = [_p, _i64, _p, _p, _i64, _i64, C.c_int, C.c_int, C.c_int, _p,
                                   _p, _p]
+    lib.or_smooth_factors.argtypes = [_p, C.c_int, _i64, _i64, _p, _i64, _p, _p]
+    lib.or_scale_columns.argtypes = [_p, C.c_int, _i64, _i64, _p, _p]
     for f in ("or_quantize_act", "or_hessian_diag", "or_quantize_weights", "or_delta_scores",
               "or_select_topk", "or_pack_weights", "or_accumulators", "or_output",
-              "or_distortion"):
+              "or_distortion", "or_smooth_factors", "or_scale_columns"):
         getattr(lib, f).restype = C.c_int
     _libs[path] = lib
     return lib
@@ -104,6 +106,40 @@ class Oracle:
         self._check(self.lib.or_quantize_act(self._ptr(x), dt, M, K, self._ptr(xq), self._ptr(sx)),
                     "quantize_act")
         return xq, sx
+
+    # -- O0
+    def smooth_factors(self, x: np.ndarray, w: np.ndarray):
+        """Per-channel migration factors (s, r = 1/s), fp32 [K] each."""
+        x = np.ascontiguousarray(x)
+        dt = 1 if x.dtype == np.uint16 else 0
+        if dt == 0:
+            x = np.ascontiguousarray(x, dtype=np.float32)
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        M, K = x.shape
+        N = w.shape[0]
+        s = np.zeros(K, np.float32)
+        r = np.zeros(K, np.float32)
+        self._check(self.lib.or_smooth_factors(self._ptr(x), dt, M, K, self._ptr(w), N, self._ptr(s),
+                                               self._ptr(r)), "smooth_factors")
+        return s, r
+
+    def scale_columns(self, a: np.ndarray, c: np.ndarray) -> np.ndarray:
+        """fp32(a[i][k] * c[k]) for an fp32 or bf16-bits (uint16) matrix."""
+        a = np.ascontiguousarray(a)
+        dt = 1 if a.dtype == np.uint16 else 0
+        if dt == 0:
+            a = np.ascontiguousarray(a, dtype=np.float32)
+        R, K = a.shape
+        out = np.zeros((R, K), np.float32)
+        self._check(self.lib.or_scale_columns(self._ptr(a), dt, R, K,
+                                              self._ptr(np.ascontiguousarray(c, dtype=np.float32)),
+                                              self._ptr(out)), "scale_columns")
+        return out
+
+    def migrate(self, x_raw: np.ndarray, w: np.ndarray):
+        """The migrated layer (X^, W^) in fp32, and (s, r)."""
+        s, r = self.smooth_factors(x_raw, w)
+        return self.scale_columns(x_raw, r), self.scale_columns(w, s), s, r
 
     # -- O4
     def hessian_diag(self, x: np.ndarray) -> np.ndarray:

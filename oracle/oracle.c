@@ -152,6 +152,45 @@ int or_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* x
 }
 
 /* ------------------------------------------------------------------------- */
+/* O0: migration of activation outliers into the weights by an equivalent      */
+/* per-channel transform (Methodology 1 starts with one, naming SmoothQuant as */
+/* an example; the pages fix no exponent, the reading here is alpha = 1/2):    */
+/*   a_k = max_m |x_mk|, b_k = max_n |w_nk|,                                   */
+/*   s_k = sqrt(a_k) / sqrt(b_k)   (fp32 square roots and division),           */
+/*   s_k = 1 when a_k or b_k is 0 (a dead channel is left alone), r_k = 1/s_k. */
+/* The migrated layer is W^ = W diag(s) and X^ = X diag(r) (both fp32, one     */
+/* rounding per element): X^ W^T = X W^T up to those roundings.                */
+/* ------------------------------------------------------------------------- */
+int or_smooth_factors(const void* x, int x_dtype, int64_t M, int64_t K, const float* w, int64_t N,
+                      float* s, float* r) {
+    if (M <= 0 || N <= 0 || K <= 0 || (x_dtype != 0 && x_dtype != 1)) return -1;
+    for (int64_t k = 0; k < K; ++k) {
+        float a = 0.0f, b = 0.0f;
+        for (int64_t m = 0; m < M; ++m) {
+            float v = fabsf(load_x(x, x_dtype, m * K + k));
+            if (v > a) a = v;
+        }
+        for (int64_t n = 0; n < N; ++n) {
+            float v = fabsf(w[n * K + k]);
+            if (v > b) b = v;
+        }
+        float sk = 1.0f;
+        if (a > 0.0f && b > 0.0f) sk = MUT(14) ? sqrtf(b) / sqrtf(a) : sqrtf(a) / sqrtf(b);
+        s[k] = sk;
+        r[k] = 1.0f / sk;
+    }
+    return 0;
+}
+
+/* out[i][k] = fp32(in[i][k] * c[k]) for an fp32 or bf16 input (rows x K) */
+int or_scale_columns(const void* in, int in_dtype, int64_t rows, int64_t K, const float* c, float* out) {
+    if (rows < 0 || K <= 0 || (in_dtype != 0 && in_dtype != 1)) return -1;
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t k = 0; k < K; ++k) out[i * K + k] = load_x(in, in_dtype, i * K + k) * c[k];
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* O4: diagonal-Hessian estimate of the input channels, h_k = mean_m x_mk^2   */
 /* ------------------------------------------------------------------------- */
 int or_hessian_diag(const void* x, int x_dtype, int64_t M, int64_t K, float* h) {

@@ -290,3 +290,44 @@ def test_quantizer_near_ties(mq, orc):
     inp = synth.Inputs(cfg, w, x, None)
     _check(mq, orc, inp, cfg.k_blocks(100), "f32")
     _check(mq, orc, inp, cfg.k_blocks(10), "bf16")
+
+
+# --------------------------------------------------------------------------- outlier migration
+MIGRATION = ["tiny", "llama3_8b_qo",
+             synth.custom_config("migrated_tiled", M=300, K=1024, N=320, bn=64, x_channel_scale=80.0)]
+
+
+@pytest.mark.parametrize("which", MIGRATION, ids=lambda c: c if isinstance(c, str) else c.name)
+def test_migrated_layer(mq, orc, which):
+    """The migration step on the GPU (factors, W^ = W diag(s), the Hessian and the
+    activation quantizer applied to x * r on the fly) and the whole path on the
+    migrated layer, against the oracle run on its own migrated X^ and W^: bit-exact
+    on s, r, W^, h, Delta, CSR, codes, scales and group sums; y within tolerance."""
+    import torch
+    inp = _inputs(which)
+    cfg = inp.cfg
+    kb = cfg.k_blocks(cfg.default_budget)
+    say(f"[parity] migrated {cfg.name} M={cfg.M} K={cfg.K} N={cfg.N} k_blocks={kb}")
+    xh, wh, s_ref, r_ref = orc.migrate(inp.x_raw(), inp.W)
+    ref = orc.forward(xh, wh, kb, cfg.group, cfg.bn, cfg.bk)
+    x = _x_dev(inp)
+    w = _to_dev(inp.W)
+    g = mq.forward_layer(x, w, kb, bn=cfg.bn, out_dtype=torch.float32, migrate=True)
+    dump = torch.empty((cfg.M, cfg.N, cfg.K // 128), dtype=torch.int32, device="cuda")
+    mq.gemm_w4a4_residual(g["xq"], g["sx"], g["wq"], g["sw"], g["row_ptr"], g["col_idx"], g["rq"], cfg.K,
+                          bn=cfg.bn, out_dtype=torch.float32, acc_dump=dump)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(g["s"]), s_ref)
+    np.testing.assert_array_equal(_np(g["r"]), r_ref)
+    np.testing.assert_array_equal(_np(g["w_hat"]), wh)
+    for k in ("h", "delta", "row_ptr", "col_idx", "sx"):
+        np.testing.assert_array_equal(_np(g[k]), ref[k], err_msg=k)
+    np.testing.assert_array_equal(xq_to_rowmajor(_np(g["xq"]), cfg.M, cfg.K), ref["xq"])
+    np.testing.assert_array_equal(wq_to_rowmajor(_np(g["wq"]), cfg.N, cfg.K), ref["wq"])
+    sw, pad = sw_to_rowmajor(_np(g["sw"]), cfg.N, cfg.K)
+    np.testing.assert_array_equal(sw, ref["sw"])
+    np.testing.assert_array_equal(rq_to_twos(_np(g["rq"])), ref["rq"])
+    np.testing.assert_array_equal(_np(dump).astype(np.int64), 14 * ref["P"].astype(np.int64) + ref["Pr"])
+    err = rel_err(_np(g["y"]), ref["y"])
+    say(f"[parity] migrated {cfg.name} y max rel err {err:.3e}")
+    assert err <= Y_TOL["f32"]

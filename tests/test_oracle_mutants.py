@@ -14,6 +14,7 @@ Each mutant is the oracle with one planted slip (oracle.c, OR_MUTANT = k):
 11 dense partial sums pair x with the neighbouring weight
 12 base error has the wrong sign
 13 activation scale absmax/8 instead of absmax/7
+14 migration factors with activation and weight ranges swapped
 The mutants are built on the CPU into a temporary folder; the pins must fail
 on every one of them.
 """
@@ -25,7 +26,7 @@ import pytest
 import oracle
 from tests import test_oracle_pins as pins
 
-MUTANTS = list(range(1, 14))
+MUTANTS = list(range(1, 15))
 PIN_FUNCS = [f for name, f in inspect.getmembers(pins, inspect.isfunction)
              if name.startswith("test_") and "orc" in inspect.signature(f).parameters]
 

@@ -402,3 +402,41 @@ def test_distortion_non_increasing_in_budget(orc):
         assert dd <= prev_d * (1 + 1e-12)       # a theorem: every Delta >= 0
         assert de <= prev_e * (1 + 1e-12)       # checked along this nested sweep
         prev_e, prev_d = de, dd
+
+
+# --------------------------------------------------------------------------- O0 migration
+def _migration_layer():
+    import synth
+    cfg = synth.custom_config("mig", M=48, K=256, N=96, bn=32, x_bf16=True, x_channel_frac=0.02,
+                              x_channel_scale=60.0)
+    inp = synth.make_inputs(cfg, seed=7)
+    inp.X_bits[:, 11] = 0          # a dead input channel
+    inp.X[:, 11] = 0.0
+    return inp
+
+
+def test_migration_is_an_equivalent_transform(orc):
+    """X^ W^T equals X W^T (float64 products of the fp32 values) up to the two
+    per-element roundings."""
+    inp = _migration_layer()
+    xh, wh, s, r = orc.migrate(inp.x_raw(), inp.W)
+    ref = inp.X.astype(np.float64) @ inp.W.astype(np.float64).T
+    got = xh.astype(np.float64) @ wh.astype(np.float64).T
+    scale = np.abs(inp.X.astype(np.float64)) @ np.abs(inp.W.astype(np.float64)).T
+    assert np.max(np.abs(got - ref) / np.maximum(scale, 1e-30)) < 3e-7
+
+
+def test_migration_balances_channel_ranges(orc):
+    """alpha = 1/2 makes every live channel's activation range equal its weight
+    range, both sqrt(max|x_k| * max|w_k|); a dead channel keeps s = r = 1."""
+    inp = _migration_layer()
+    xh, wh, s, r = orc.migrate(inp.x_raw(), inp.W)
+    a = np.abs(inp.X).max(axis=0).astype(np.float64)
+    b = np.abs(inp.W).max(axis=0).astype(np.float64)
+    live = (a > 0) & (b > 0)
+    target = np.sqrt(a * b)
+    np.testing.assert_allclose(np.abs(xh).max(axis=0)[live], target[live], rtol=4e-7)
+    np.testing.assert_allclose(np.abs(wh).max(axis=0)[live], target[live], rtol=4e-7)
+    assert s[11] == 1.0 and r[11] == 1.0 and not live[11]
+    # the outlier channels' range shrinks by sqrt(a/b): they migrate into the weights
+    assert np.abs(xh).max() < 0.2 * np.abs(inp.X).max()
