@@ -47,7 +47,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 F8_PEAK_TOPS = 5000.0           # MI355X dense fp8 (and int8) MFMA
 ROTATE_BYTES = 640 << 20        # > 2 x (256 MB Infinity Cache + 8 x 4 MB L2)
 GEMM_SRC = os.path.join("dense_sparse_bit_amd", "csrc", "gemm.hip")
-TRAFFIC_SUMMARY = os.path.join("profiles", "gemm_fused_qwen3_14b_prefill_hbm_traffic.txt")
+TRAFFIC_SUMMARY = os.path.join("profiles", "gemm_prefill_qwen3_14b_counters.txt")
 
 # workloads measured beside the headline in one default run: (config, budgets in %)
 LEGS = [("llama3_8b_qo", (10,)),
@@ -392,7 +392,7 @@ def _counter_means(db_path, counter):
     return {k: sum(v) / len(v) for k, v in per.items()}, calib
 
 
-def counters_summary(db_paths, title, commands):
+def counters_summary(db_paths, title, commands, only="k_gemm"):
     """Mean per dispatch of every counter in the given rocprofv3 --pmc databases, for
     the library's kernels; FETCH_SIZE and WRITE_SIZE are also scaled to bytes by what
     they read for the calibration copy (CALIB_COPY_BYTES read and written)."""
@@ -404,7 +404,7 @@ def counters_summary(db_paths, title, commands):
         for c in names:
             per, calib = _counter_means(path, c)
             for k, v in per.items():
-                if "mq::" in k:
+                if "mq::" in k and only in k:
                     table.setdefault(k, {})[c] = v
             if c in ("FETCH_SIZE", "WRITE_SIZE") and calib:
                 big = max(g for g, _ in calib)
@@ -524,6 +524,7 @@ def main():
     ap.add_argument("--profile-summary", metavar="DB", help="print a rocprofv3 kernel-trace summary")
     ap.add_argument("--counters-summary", nargs="+", metavar="DB",
                     help="print per-kernel counter means from rocprofv3 --pmc databases")
+    ap.add_argument("--kernels", default="k_gemm", help="counters summary: kernels whose name holds this")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
@@ -531,7 +532,7 @@ def main():
         print(profile_summary(args.profile_summary, args.title, " ; ".join(args.command)))
         return
     if args.counters_summary:
-        print(counters_summary(args.counters_summary, args.title, args.command))
+        print(counters_summary(args.counters_summary, args.title, args.command, args.kernels))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path has "
