@@ -615,6 +615,372 @@ __global__ __launch_bounds__(256, DUMP ? 1 : 2) void k_gemm_prefill(GemmArgs a) 
         }
 }
 
+// Workgroup b of a grid of T runs on XCD b % 8 (the dispatcher deals workgroups
+// round-robin over the eight XCDs). Give XCD x the contiguous tile range
+// [x q + min(x, r), ...) of q + (x < r) tiles (q = T / 8, r = T % 8), walked in
+// order: a bijection of [0, T) that keeps neighbouring tiles on one L2.
+__device__ __forceinline__ int xcd_tile(int b, int T) {
+    const int q = T >> 3, r = T & 7, x = b & 7, l = b >> 3;
+    return x * q + min(x, r) + l;
+}
+
+// ===========================================================================
+// Wide prefill kernel, M > 32: a workgroup of NWN waves owns 96 tokens x 64 NWN
+// output columns, and each wave all 96 tokens of its own 64 columns (3 x 2 tiles
+// of 32 x 32, 32 x 32 x 64 fp8 MFMAs), one 128-wide K group per step.
+//   * Every weight tile is loaded and widened to fp8 by exactly one wave (straight
+//     from memory into registers, a group ahead of its use).
+//   * Every activation tile is loaded and widened once per workgroup: the waves
+//     split the group's 96 x 64-byte run, widen their part and store it in LDS in
+//     MFMA lane order; each operand read is then two conflict-free 1 KB LDS reads.
+//     One barrier per group.
+//   * Per group and tile: P from two MFMAs (one per 64-input half), then
+//     acc += fp32(s) * 2^18 * P.
+//   * A half of a group holding a chosen block of the wave's block row (a scalar
+//     branch: a wave's 64 columns lie in one block row) adds one MFMA per tile on
+//     that half's activation operands, acc += fp32(s / 14) * 2^18 * Pr. The block's
+//     codes are fetched during the group's step and multiplied at the start of the
+//     next one, so their latency is hidden; LDS therefore keeps three stages of
+//     activation operands (the group being finished, the current one, the next).
+// Per group and wave the VALU work is the 96 dequantizing FMAs, the widening of
+// 4 KB of weight nibbles and 1/NWN of the activation widening, against 12 MFMAs:
+// close to balanced, so two waves per SIMD keep the MFMA pipe fed. 96 rows (not
+// 128) leave the registers for the prefetched operands without spilling.
+// ===========================================================================
+constexpr int kMT = 3;          // 32-row MFMA tiles per wave
+constexpr int kWM = 32 * kMT;   // tokens per workgroup tile
+
+struct WideRes {
+    uint4 r[2];        // codes of the first chosen half [column tile j] (zeros if none)
+    int rmask;         // bit h: half h holds a chosen block (wave-uniform)
+    int jb1;           // CSR position of half 1's block, or -1
+};
+
+template <int NWN, bool RES, bool DUMP, int OUTMODE>
+__global__ __launch_bounds__(64 * NWN, DUMP ? 1 : 2) void k_gemm_wide(GemmArgs a, int n_begin, int tiles_n) {
+    constexpr int kRuns = kWM / 16;                   // 1 KB activation runs per group
+    constexpr int kXU = (kRuns + NWN - 1) / NWN;      // runs per wave (run wave + NWN u)
+    constexpr int kStages = RES ? 3 : 2;
+    // [stage][32-row tile][half 2][part 2][lane 64][16 B]
+    __shared__ __align__(16) uint8_t xs[kStages][kMT][2][2][1024];
+    __shared__ __align__(16) uint8_t xspare[(kXU * NWN > kRuns) ? 2048 : 16];
+    __shared__ int tab[RES ? NWN * 2 * kMaxGroups : 1];     // per wave: column block -> CSR position
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lc = lane & 31, lh = lane >> 5;
+    // Tile order: workgroup b runs on XCD b % 8, and each XCD takes a contiguous
+    // range of tiles ordered column-tile-major, so the workgroups an XCD runs at
+    // one time share column tiles (weights) and all token tiles (activations) in
+    // that XCD's L2.
+    const int tiles_m = (a.M + kWM - 1) / kWM;
+    const int t = xcd_tile(static_cast<int>(blockIdx.x), tiles_m * tiles_n);
+    const int m0 = (t % tiles_m) * kWM;
+    const int n0 = n_begin + (t / tiles_m) * (64 * NWN);
+    const int G = a.K / kGroup, G4 = (G + 3) / 4, nbc = 2 * G;
+    const int wc0 = n0 + wave * 64;                                   // the wave's first column
+
+    // weights of the wave's 64 columns: four 16-row tiles; tiles past N read zero
+    // (one resource per pair of tiles, so that the range check, which covers the
+    // per-lane offset, alone decides which lanes read zeros)
+    const int wtiles = max(0, min(4, (a.N - wc0) / 16));
+    __amdgpu_buffer_rsrc_t rb[2], rs[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int t = max(0, min(2, wtiles - 2 * j));
+        rb[j] = buf_rsrc_uniform(a.wq + static_cast<int64_t>((wc0 >> 4) + 2 * j) * G * 1024,
+                                 static_cast<uint32_t>(t) * G * 1024u);
+        rs[j] = buf_rsrc_uniform(a.sw + static_cast<int64_t>((wc0 >> 4) + 2 * j) * G4 * 64,
+                                 static_cast<uint32_t>(t) * G4 * 128u);
+    }
+    // lane's offset for column tile j, half h of group g: tile 2j + lc/16, row lc%16,
+    // chunk 2h + lh, i.e. a per-lane part plus a wave-uniform part (scalar offset)
+    const uint32_t bvo = static_cast<uint32_t>(lc >> 4) * G * 1024u + static_cast<uint32_t>((lh * 16 + (lc & 15)) * 16);
+    // the lane's fp16 group scale of column tile j: element (tile, g/4, row, g%4)
+    const uint32_t svo = (static_cast<uint32_t>(lc >> 4) * G4 * 64u + (lc & 15) * 4u) * 2u;
+    auto load_scale = [&](int g, int j) __attribute__((always_inline)) -> uint32_t {
+        const uint32_t gc = static_cast<uint32_t>(min(g, G - 1));
+        return __builtin_amdgcn_raw_buffer_load_b16(rs[j], svo, (gc >> 2) * 128u + (gc & 3) * 2u, 0);
+    };
+
+    // the wave's zipper table (its 64 columns lie in one block row), built by the
+    // wave alone: a wavefront's LDS operations complete in issue order
+    int* wt = tab + (RES ? wave * nbc : 0);
+    __amdgpu_buffer_rsrc_t rr = buf_rsrc_uniform(a.wq, 0u);
+    const __amdgpu_buffer_rsrc_t rnull = buf_rsrc_uniform(a.wq, 0u);   // reads zeros
+    int wlo = 0, rbase = 0;
+    if (RES) {
+        for (int i = lane; i < nbc; i += 64) wt[i] = -1;
+        __builtin_amdgcn_wave_barrier();
+        if (wc0 < a.N) {
+            const int brw = wc0 / a.bn;
+            wlo = clampi(a.row_ptr[brw], 0, a.nnz);
+            const int whi = clampi(a.row_ptr[brw + 1], wlo, a.nnz);
+            for (int i = wlo + lane; i < whi; i += 64) {
+                const int kb = a.col_idx[i];
+                if (kb >= 0 && kb < nbc) wt[kb] = i;
+            }
+            rr = buf_rsrc_uniform(whi > wlo ? a.rq + static_cast<int64_t>(wlo) * a.bn * 32 : a.wq,
+                                  static_cast<uint32_t>(whi - wlo) * static_cast<uint32_t>(a.bn) * 32u);
+            rbase = wc0 % a.bn;   // the wave's first row inside its block
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // activation fill: the wave's 1 KB runs of a group (rows R0 + 16 u + lane % 16,
+    // 16-byte chunk lane / 16), stored widened at their MFMA operand positions
+    // row of run r: 16 r + lane % 16, chunk kc = lane / 16; destination: 32-row
+    // tile row / 32, half kc / 2, operand lane row % 32 + 32 (kc % 2)
+    const uint32_t xvo = static_cast<uint32_t>(lane & 15) * 64u + static_cast<uint32_t>(lane >> 4) * 16u;
+    const int kc = lane >> 4;
+    const int xdl = ((kc >> 1) * 2 * 64 + (lane & 15) + 32 * (kc & 1)) * 16;   // per-lane part
+    auto xdst = [&](int u) __attribute__((always_inline)) {
+        const int row = 16 * (wave + NWN * u);                   // wave-uniform part of the row
+        return xdl + ((row >> 5) * 4 * 64 + (row & 31)) * 16;
+    };
+    auto load_x = [&](int g, uint4 (&L)[kXU]) __attribute__((always_inline)) {
+        const int gc = min(g, G - 1);
+#pragma unroll
+        for (int u = 0; u < kXU; ++u) {
+            // this run's 16 rows (rows past M, and runs past the tile, read zero)
+            const int r0 = 16 * (wave + NWN * u);
+            const __amdgpu_buffer_rsrc_t rx = buf_rsrc_uniform(
+                a.xq + (static_cast<int64_t>(gc) * a.M + m0 + r0) * 64,
+                static_cast<uint32_t>(r0 < kWM ? max(0, min(a.M - m0 - r0, 16)) : 0) * 64u);
+            L[u] = buf_load16(rx, xvo);
+        }
+    };
+    auto store_x = [&](const uint4 (&L)[kXU], int st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kXU; ++u) {
+            // a run past the tile (zeros) is written to a spare area: no branch
+            const v8i v = f8_operand(L[u]);
+            uint8_t* d = wave + NWN * u < kRuns ? &xs[st][0][0][0][0] + xdst(u) : &xspare[lane * 16];
+            *reinterpret_cast<v4i*>(d) = v4i{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<v4i*>(d + 1024) = v4i{v[4], v[5], v[6], v[7]};
+        }
+    };
+    auto load_w = [&](int g, uint4 (&B)[2][2]) __attribute__((always_inline)) {
+        const uint32_t gc = static_cast<uint32_t>(min(g, G - 1));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) B[j][h] = buf_load16s(rb[j], bvo, h * 512u + gc * 1024u);
+    };
+    // the codes of column tile j of block jb: row rbase + 32 j + lc of the block, bytes
+    // 16 lh .. 16 lh + 15 (a per-lane part and a wave-uniform part); no block reads zeros
+    const uint32_t rvo = static_cast<uint32_t>(lc * 32 + lh * 16);
+    auto load_codes = [&](int jb, int j) __attribute__((always_inline)) {
+        const uint32_t so = static_cast<uint32_t>(((jb - wlo) * a.bn + rbase + 32 * j) * 32);
+        return buf_load16s(jb >= 0 ? rr : rnull, rvo, jb >= 0 ? so : 0u);
+    };
+    auto a_operand = [&](int st, int i, int h) __attribute__((always_inline)) {
+        const uint8_t* base = &xs[st][i][h][0][0];
+        const v4i lo = *reinterpret_cast<const v4i*>(base + lane * 16);
+        const v4i hi = *reinterpret_cast<const v4i*>(base + 1024 + lane * 16);
+        return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto dump_idx = [&](int i, int j, int r, int g) __attribute__((always_inline)) -> int64_t {
+        const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int nn = wc0 + j * 32 + lc;
+        return (m < a.M && nn < a.N) ? (static_cast<int64_t>(m) * a.N + nn) * G + g : -1;
+    };
+
+    v16f acc[kMT][2];
+#pragma unroll
+    for (int i = 0; i < kMT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // base pass of group g: operands of stage st, weight nibbles Bn, scale bits sb
+    auto compute = [&](int g, int st, const uint4 (&Bn)[2][2], const uint32_t (&sb)[2]) __attribute__((always_inline)) {
+        float fs[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fs[j] = f16_bits_to_f32(static_cast<uint16_t>(sb[j])) * kF8Unit;
+        v8i bop[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) bop[j][h] = f8_operand(Bn[j][h]);
+#pragma unroll
+        for (int i = 0; i < kMT; ++i) {
+            const v8i a0 = a_operand(st, i, 0), a1 = a_operand(st, i, 1);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const v16f z = {};
+                v16f p = mfma32_f8(a0, bop[j][0], z);
+                p = mfma32_f8(a1, bop[j][1], p);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(fs[j], p[r], acc[i][j][r]);
+                if (DUMP) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int64_t d = dump_idx(i, j, r, g);
+                        if (d >= 0) a.acc_dump[d] = 14 * static_cast<int>(p[r] * kF8Unit);
+                    }
+                }
+            }
+        }
+    };
+    // the chosen halves of group g and the first one's codes (an absent block reads
+    // zeros: the load is issued every step, so no register copy waits on it)
+    auto load_res = [&](int g, WideRes& R) __attribute__((always_inline)) {
+        const int jb0 = __builtin_amdgcn_readfirstlane(wt[2 * g]);
+        const int jb1 = __builtin_amdgcn_readfirstlane(wt[2 * g + 1]);
+        R.rmask = (jb0 >= 0 ? 1 : 0) | (jb1 >= 0 ? 2 : 0);
+        R.jb1 = jb1;
+        const int jb = jb0 >= 0 ? jb0 : jb1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) R.r[j] = load_codes(jb, j);
+    };
+    // residual pass of half h of group g (stage st): one MFMA per tile
+    auto res_half = [&](int g, int st, int h, const uint4 (&codes)[2], const float (&fr)[2]) __attribute__((always_inline)) {
+        v8i ra[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) ra[j] = f8_operand(codes[j]);
+#pragma unroll
+        for (int i = 0; i < kMT; ++i) {
+            const v8i aa = a_operand(st, i, h);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const v16f z = {};
+                const v16f pr = mfma32_f8(aa, ra[j], z);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(fr[j], pr[r], acc[i][j][r]);
+                if (DUMP) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int64_t d = dump_idx(i, j, r, g);
+                        if (d >= 0) a.acc_dump[d] += static_cast<int>(pr[r] * kF8Unit);
+                    }
+                }
+            }
+            // keep the scheduler from hoisting every tile's MFMA (and its 16 result
+            // registers) above the dequantization of the earlier tiles
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // residual pass of group g: the first chosen half's codes were fetched a step
+    // earlier; a second chosen half (rare) is fetched and used here
+    auto residual = [&](int g, int st, const WideRes& R, const uint32_t (&sb)[2]) __attribute__((always_inline)) {
+        float fr[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fr[j] = div14(f16_bits_to_f32(static_cast<uint16_t>(sb[j]))) * kF8Unit;
+        res_half(g, st, (R.rmask & 1) ? 0 : 1, R.r, fr);
+        if (R.rmask == 3) {
+            uint4 c[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) c[j] = load_codes(R.jb1, j);
+            res_half(g, st, 1, c, fr);
+        }
+    };
+
+    // Instruction order of a step's base pass (the scheduler otherwise issues all
+    // MFMAs back to back and all dequantizing FMAs after them, so the VALU and the
+    // MFMA pipe of a wave take turns): the next group's loads first, then the
+    // weight widening, then each row of tiles' LDS reads and MFMAs with VALU work
+    // between the MFMAs (the widening of column tile 1 and of the next group's
+    // activations under row 0, the previous row's FMAs under the later rows).
+    auto schedule_step = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_group_barrier(0x0020, 6, 0);       // loads of group g + 1
+        __builtin_amdgcn_sched_group_barrier(0x0002, 24, 0);      // widen column tile 0
+        __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);       // row 0 operands
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x0002, 12, 0);
+        }
+#pragma unroll
+        for (int i = 1; i < kMT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x0002, 8, 0);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x0002, 40, 0);      // the last row's FMAs
+        __builtin_amdgcn_sched_group_barrier(0x0200, 2 * kXU, 0); // activation stores
+        __builtin_amdgcn_sched_group_barrier(0x0020, kXU, 0);     // loads of group g + 2
+    };
+
+    // Pipeline: step g (stage g % kStages) first finishes group g - 1's residual
+    // pass (its codes were fetched during step g - 1), then fetches group g + 2's
+    // weights and scales and group g's residual codes, multiplies group g with the
+    // weights fetched during step g - 2, widens group g + 1's activations (fetched
+    // during step g - 1) into the next stage and fetches group g + 2's. Unrolled by
+    // three so that the weight and scale registers rotate without copies.
+    uint4 B0[2][2], B1[2][2], B2[2][2], X[kXU];
+    uint32_t S0[2], S1[2], S2[2];
+    WideRes R;
+    R.rmask = 0;
+    R.jb1 = -1;
+    load_x(0, X);
+    load_w(0, B0);
+    load_w(1, B1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        S0[j] = load_scale(0, j);
+        S1[j] = load_scale(1, j);
+    }
+    store_x(X, 0);
+    load_x(1, X);
+    __syncthreads();
+    // step g: weights and scales of group g in Bc/Sc (fetched two steps earlier);
+    // group g + 2's go to Bn/Sn, which held group g - 1's
+    auto step = [&](int g, const uint4 (&Bc)[2][2], uint4 (&Bn)[2][2], const uint32_t (&Sc)[2],
+                    uint32_t (&Sn)[2]) __attribute__((always_inline)) {
+        const int st = g % kStages;
+        if (RES && R.rmask) {
+            __asm__ volatile("" ::: "memory");
+            residual(g - 1, (g + kStages - 1) % kStages, R, Sn);   // Sn still holds group g - 1's scales
+        }
+        load_w(g + 2, Bn);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) Sn[j] = load_scale(g + 2, j);
+        if (RES) load_res(g, R);
+        compute(g, st, Bc, Sc);
+        store_x(X, (g + 1) % kStages);
+        load_x(g + 2, X);
+        schedule_step();
+        __syncthreads();
+    };
+    for (int g = 0; g < G; g += 3) {
+        step(g, B0, B2, S0, S2);
+        if (g + 1 >= G) break;
+        step(g + 1, B1, B0, S1, S0);
+        if (g + 2 >= G) break;
+        step(g + 2, B2, B1, S2, S1);
+    }
+    if (RES && R.rmask) residual(G - 1, (G - 1) % kStages, R, (G - 1) % 3 == 0 ? S0 : ((G - 1) % 3 == 1 ? S1 : S2));
+
+    // Epilogue: y = acc * sx, bf16 or fp32 (rows past M and columns past N skipped)
+    const __amdgpu_buffer_rsrc_t rsx = buf_rsrc_uniform(a.sx + m0, static_cast<uint32_t>(max(0, min(kWM, a.M - m0))) * 4u);
+#pragma unroll
+    for (int i = 0; i < kMT; ++i) {
+        float sxi[16];
+        if (OUTMODE == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                sxi[r] = __builtin_bit_cast(float, buf_load4(rsx, static_cast<uint32_t>(i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)) * 4u));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int nn = wc0 + j * 32 + lc;
+            if (nn >= a.N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (m >= a.M) continue;
+                const int64_t idx = static_cast<int64_t>(m) * a.N + nn;
+                if (OUTMODE == 1) a.ws[idx] = acc[i][j][r];
+                else if (a.y_bf16) static_cast<uint16_t*>(a.y)[idx] = f32_to_bf16_bits(acc[i][j][r] * sxi[r]);
+                else static_cast<float*>(a.y)[idx] = acc[i][j][r] * sxi[r];
+            }
+        }
+    }
+}
+
 // ===========================================================================
 // Second kernel of the separate-kernel alternative: re-reads the activations,
 // computes each chosen block's residual product, adds it to the dense partial
@@ -680,10 +1046,19 @@ static hipError_t go_prefill(const GemmArgs& a, hipStream_t st) {
 }
 
 template <bool RES, bool DUMP, int OUT>
+static hipError_t go_wide(const GemmArgs& a, hipStream_t st) {
+    constexpr int NWN = 4;
+    const int tiles_n = (a.N + 64 * NWN - 1) / (64 * NWN);
+    const int tiles = ((a.M + kWM - 1) / kWM) * tiles_n;
+    k_gemm_wide<NWN, RES, DUMP, OUT><<<dim3(tiles), dim3(64 * NWN), 0, st>>>(a, 0, tiles_n);
+    return hipGetLastError();
+}
+
+template <bool RES, bool DUMP, int OUT>
 static hipError_t go(const GemmArgs& a, hipStream_t st) {
     if (a.M <= 16) return go_decode<1, RES, DUMP, OUT>(a, st);
     if (a.M <= 32) return go_decode<2, RES, DUMP, OUT>(a, st);
-    return go_prefill<RES, DUMP, OUT>(a, st);
+    return go_wide<RES, DUMP, OUT>(a, st);
 }
 
 // ---------------------------------------------------------------------------

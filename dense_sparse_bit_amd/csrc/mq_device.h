@@ -207,6 +207,11 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// the same with a wave-uniform byte offset added in the instruction (scalar operand)
+__device__ __forceinline__ uint4 buf_load16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
 }
