@@ -127,7 +127,8 @@ class Layer:
         mq, cfg = self.mq, self.cfg
         rp, ci, _ = mq.select_blocks(self.w, self.h, k_blocks, bn=cfg.bn, return_delta=False)
         wq, sw, rq = mq.pack_weights(self.w, rp, ci, bn=cfg.bn)
-        return dict(wq=wq, sw=sw, rq=rq, row_ptr=rp, col_idx=ci)
+        rmap = mq.block_map(rp, ci, cfg.N, cfg.K, bn=cfg.bn)
+        return dict(wq=wq, sw=sw, rq=rq, row_ptr=rp, col_idx=ci, rmap=rmap)
 
     def copies(self, packed, nbytes):
         n = max(2, min(256, -(-ROTATE_BYTES // max(nbytes, 1))))
@@ -149,6 +150,11 @@ def bench_variants(mq, torch, layer, k_blocks, calls, bf16=True):
 
     def fused(i):
         s = sets[i % n]
+        mq.gemm_w4a4_residual(xq, sx, s["wq"], s["sw"], s["row_ptr"], s["col_idx"], s["rq"], K, bn=bn, y=y,
+                              rmap=s["rmap"])
+
+    def fused_csr(i):
+        s = sets[i % n]
         mq.gemm_w4a4_residual(xq, sx, s["wq"], s["sw"], s["row_ptr"], s["col_idx"], s["rq"], K, bn=bn, y=y)
 
     def dense(i):
@@ -161,7 +167,7 @@ def bench_variants(mq, torch, layer, k_blocks, calls, bf16=True):
                                   bn=bn, y=y, ws=wsb)
 
     out = {}
-    for name, fn in (("dense", dense), ("fused", fused), ("separate", separate)):
+    for name, fn in (("dense", dense), ("fused", fused), ("fused_csr", fused_csr), ("separate", separate)):
         fn(calls - 1)
         torch.cuda.synchronize()
         y_eager = y.clone()
@@ -196,8 +202,10 @@ def leg_record(cfg, pct, k_blocks, t):
     rec = {"workload": cfg.name, "M": cfg.M, "K": cfg.K, "N": cfg.N, "bn": cfg.bn, "budget_pct": pct,
            "k_blocks": k_blocks, "bound": roofline_kind(cfg), "bytes": fb, "ops": fo,
            "fused": one(t["fused"], fb, fo), "dense": one(t["dense"], db, do),
+           "fused_csr": one(t["fused_csr"], fb, fo),
            "separate": one(t["separate"], fb, fo),
            "overhead_vs_dense": round(t["fused"] / t["dense"] - 1, 4),
+           "overhead_csr_vs_dense": round(t["fused_csr"] / t["dense"] - 1, 4),
            "separate_overhead_vs_dense": round(t["separate"] / t["dense"] - 1, 4)}
     if "bf16_matmul" in t:
         rec["bf16_matmul_us"] = round(t["bf16_matmul"], 3)
@@ -247,7 +255,8 @@ def bench_step(mq, torch, layer, k_blocks, steps, warmup):
 
     def gemm(i):
         s = sets[i % n]
-        mq.gemm_w4a4_residual(xq, sx, s["wq"], s["sw"], s["row_ptr"], s["col_idx"], s["rq"], K, bn=bn, y=y)
+        mq.gemm_w4a4_residual(xq, sx, s["wq"], s["sw"], s["row_ptr"], s["col_idx"], s["rq"], K, bn=bn, y=y,
+                              rmap=s["rmap"])
 
     def quant(i):
         mq.quantize_act(xs[i % nx], xq=xq, sx=sx)
@@ -343,7 +352,7 @@ def pmc_pass(mq, torch, cfg, k_blocks, calls=5):
     y = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device="cuda")
     for _ in range(calls):
         mq.gemm_w4a4_residual(layer.xq, layer.sx, p["wq"], p["sw"], p["row_ptr"], p["col_idx"], p["rq"],
-                              cfg.K, bn=cfg.bn, y=y)
+                              cfg.K, bn=cfg.bn, y=y, rmap=p["rmap"])
     for _ in range(calls):
         mq.gemm_w4a4_dense(layer.xq, layer.sx, p["wq"], p["sw"], cfg.K, y=y)
     src = torch.ones(CALIB_COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -482,7 +491,7 @@ def sweep(mq, torch, calls):
             for lay, p, y, _, _ in layers:
                 mq.quantize_act(lay.x, xq=lay.xq, sx=lay.sx)
                 mq.gemm_w4a4_residual(lay.xq, lay.sx, p["wq"], p["sw"], p["row_ptr"], p["col_idx"], p["rq"],
-                                      lay.cfg.K, bn=64, y=y)
+                                      lay.cfg.K, bn=64, y=y, rmap=p["rmap"])
 
         def dense_only(i):
             for lay, p, y, _, _ in layers:
@@ -595,7 +604,7 @@ def main():
         achieved, peak, unit = ops / st["gemm_us"] / 1e6, F8_PEAK_TOPS, "TOPS"
     else:
         achieved, peak, unit = gemm_bytes(cfg, k_blocks) / st["gemm_us"] / 1e3, HBM_PEAK_GBS, "GB/s"
-    kname = "k_gemm_prefill<true, false, 0>" if cfg.M > 32 else "k_gemm_decode"
+    kname = "k_gemm_wide<4, true, false, 0>" if cfg.M > 32 else "k_gemm_decode"
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -621,7 +630,7 @@ def main():
                    "k_blocks": k_blocks, "step": "quantize_act -> gemm_w4a4_residual"},
         "roofline": {"kernel": kname, "bound": kind, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": traffic_from_profile("k_gemm_prefill<true, false" if cfg.M > 32 else "k_gemm_decode<"),
+                     "traffic": traffic_from_profile("k_gemm_wide<4, true, false" if cfg.M > 32 else "k_gemm_decode<"),
                      "per_launch": {"ops": ops, "bytes": gemm_bytes(cfg, k_blocks), "us": round(st["gemm_us"], 3)},
                      "hbm_GBs": round(gemm_bytes(cfg, k_blocks) / st["gemm_us"] / 1e3, 1),
                      "traffic_source": TRAFFIC_SUMMARY + " (rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled "

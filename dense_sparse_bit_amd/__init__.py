@@ -43,6 +43,9 @@ _SIGS = {
     "mq_gemm_w4a4_residual": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
                               _p, _int, _p, _p],
     "mq_gemm_w4a4_dense": [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p, _int, _p, _p],
+    "mq_block_map": [_p, _p, _i64, _i64, _i64, _int, _int, _p, _p],
+    "mq_gemm_w4a4_residual_mapped": [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
+                                     _p, _int, _p, _p],
     "mq_gemm_residual_separate": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int,
                                   _int, _p, _int, _p, _p],
 }
@@ -371,15 +374,38 @@ def _dump_checks(acc_dump, M, N, K):
         _buf(acc_dump, "acc_dump", 4 * M * N * (K // GROUP), _I32)
 
 
+def block_map(row_ptr, col_idx, N: int, K: int, bn: int = 64, bk: int = BK, out=None, stream=None):
+    """Dense block map int32 [N/bn][K/bk] of a CSR selection: the CSR position of
+    each chosen block, -1 elsewhere."""
+    nnz = _csr_checks(row_ptr, col_idx, N, bn)
+    if K <= 0 or K % bk or N <= 0 or N % bn:
+        raise ValueError(f"blocks {bn}x{bk} do not tile a {N}x{K} layer")
+    rmap = torch.empty((N // bn, K // bk), dtype=torch.int32, device=row_ptr.device) if out is None \
+        else _buf(out, "rmap", 4 * (N // bn) * (K // bk), _I32)
+    _on_device(row_ptr=row_ptr, col_idx=col_idx if nnz else None, rmap=rmap)
+    _call("mq_block_map", _ptr(row_ptr), _ptr(col_idx) if nnz else None, nnz, N, K, bn, bk, _ptr(rmap),
+          _stream(stream))
+    return rmap
+
+
 def gemm_w4a4_residual(xq, sx, wq, sw, row_ptr, col_idx, rq, K: int, bn: int = 64,
-                       out_dtype=torch.bfloat16, y=None, acc_dump=None, stream=None):
-    """Fused dense + sparse-residual W4A4 GEMM. acc_dump: optional int32 [M][N][K/128]."""
+                       out_dtype=torch.bfloat16, y=None, acc_dump=None, stream=None, rmap=None):
+    """Fused dense + sparse-residual W4A4 GEMM. acc_dump: optional int32 [M][N][K/128].
+    rmap: optional block_map(row_ptr, col_idx, ...) of the same selection; the call
+    then finds the blocks through it (mq_gemm_w4a4_residual_mapped, same bits)."""
     M, N = _gemm_operands(xq, sx, wq, sw, K)
     nnz = _csr_checks(row_ptr, col_idx, N, bn)
     if nnz:
         _buf(rq, "rq", nnz * bn * BK // 2, _U8, 16)
     y = _out_checks(y, M, N, out_dtype, wq.device)
     _dump_checks(acc_dump, M, N, K)
+    if rmap is not None:
+        _buf(rmap, "rmap", 4 * (N // bn) * (K // BK), _I32)
+        _on_device(xq=xq, sx=sx, wq=wq, sw=sw, rmap=rmap, rq=rq if nnz else None, y=y, acc_dump=acc_dump)
+        _call("mq_gemm_w4a4_residual_mapped", _ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(rmap),
+              _ptr(rq) if nnz else None, nnz, M, N, K, GROUP, bn, BK, _ptr(y), _y_dtype(y.dtype),
+              _ptr(acc_dump), _stream(stream))
+        return y
     _on_device(xq=xq, sx=sx, wq=wq, sw=sw, row_ptr=row_ptr, col_idx=col_idx if nnz else None,
                rq=rq if nnz else None, y=y, acc_dump=acc_dump)
     _call("mq_gemm_w4a4_residual", _ptr(xq), _ptr(sx), _ptr(wq), _ptr(sw), _ptr(row_ptr),

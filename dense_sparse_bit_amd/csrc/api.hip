@@ -68,6 +68,7 @@ mq::GemmArgs make_args(const uint8_t* xq, const float* sx, const uint8_t* wq, co
     a.sw = sw;
     a.row_ptr = row_ptr;
     a.col_idx = col_idx;
+    a.rmap = nullptr;
     a.rq = rq;
     a.nnz = static_cast<int>(nnz);
     a.M = static_cast<int>(M);
@@ -230,6 +231,32 @@ int mq_gemm_w4a4_residual(const uint8_t* xq, const float* sx, const uint8_t* wq,
     if (M == 0) return MQ_OK;
     const mq::GemmArgs a = make_args(xq, sx, wq, sw, row_ptr, col_idx, rq, nnz, M, N, K, bn, y, y_dtype,
                                      acc_dump, nullptr);
+    return hip_status(mq::launch_gemm(a, mq::GemmKind::Fused, static_cast<hipStream_t>(stream)));
+}
+
+int mq_block_map(const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz, int64_t N, int64_t K,
+                 int bn, int bk, int32_t* rmap, void* stream) {
+    int rc = check_layer(N, K, mq::kGroup, bn, bk);
+    if (rc) return rc;
+    if (nnz < 0 || nnz > (N / bn) * (K / bk) || !row_ptr || !rmap || (nnz > 0 && !col_idx))
+        return MQ_ERR_INVALID_ARG;
+    return hip_status(mq::launch_block_map(row_ptr, col_idx, nnz, N, K, bn, rmap, static_cast<hipStream_t>(stream)));
+}
+
+int mq_gemm_w4a4_residual_mapped(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint16_t* sw,
+                                 const int32_t* rmap, const uint8_t* rq, int64_t nnz, int64_t M, int64_t N,
+                                 int64_t K, int group, int bn, int bk, void* y, int y_dtype, int32_t* acc_dump,
+                                 void* stream) {
+    int rc = check_gemm(xq, sx, wq, sw, M, N, K, group, bn, bk, y, y_dtype);
+    if (rc) return rc;
+    if (nnz < 0 || nnz > (N / bn) * (K / bk) || !rmap || (nnz > 0 && (!rq || !aligned16(rq))))
+        return MQ_ERR_INVALID_ARG;
+    // the kernels address the whole payload with 32-bit byte offsets
+    if (nnz * bn * (bk / 2) > (int64_t(1) << 31)) return MQ_ERR_UNSUPPORTED;
+    if (M == 0) return MQ_OK;
+    mq::GemmArgs a = make_args(xq, sx, wq, sw, nullptr, nullptr, rq, nnz, M, N, K, bn, y, y_dtype, acc_dump,
+                               nullptr);
+    a.rmap = rmap;
     return hip_status(mq::launch_gemm(a, mq::GemmKind::Fused, static_cast<hipStream_t>(stream)));
 }
 

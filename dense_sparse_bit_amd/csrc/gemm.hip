@@ -5,19 +5,24 @@
 // a tiled pipeline, so activations are not reloaded and partial outputs are not
 // merged by a second kernel. Methodology 1 fixes both parts at 4 bits.
 //
-// Data flow per 128-wide K group g (the weight scale group):
-//   * base nibbles wq and activation nibbles xq arrive as 16-byte vector loads,
-//     each wavefront load one contiguous 1 KB run (tiled wq, group-major xq);
-//   * both are widened to int8 operands of v_mfma_i32_16x16x64_i8 (gfx950 has no
-//     int4 MFMA);
-//   * the output rows' CSR list of residual blocks is walked in step with g (the
-//     "zipper"); in a group holding a chosen block the weight operand becomes
-//     14*q + r per element, so the residual rides in the same MFMAs and the same
-//     int32 accumulator, which then holds T = 14*P + Pr exactly;
-//   * at the end of the group the exact int32 sum is dequantized into fp32:
-//     acc += s/256 * (256 P)      (dense group, both operands carry a x16 factor)
-//     acc += s_r/16 * (16 T)      (residual group, s_r = fp32(s/14))
-//   * the epilogue multiplies by the token scale sx and stores bf16 or fp32.
+// Arithmetic per 128-wide K group g (the weight scale group):
+//   * base nibbles wq and activation nibbles xq arrive as 16-byte vector loads
+//     (tiled wq and group-major xq: one contiguous 1 KB run per wavefront load);
+//   * two masks turn a packed code word into fp8 (e4m3) MFMA operand bytes: code
+//     c in [-7, 7] is the subnormal c * 2^-9 (see mq_device.h). gfx950 has no
+//     int4 MFMA; the fp8 ones take 128 (16 x 16) or 64 (32 x 32) inputs per
+//     instruction at the int8 rate and return fp32;
+//   * every product is a multiple of 2^-18 and a group sum is at most
+//     128 * 49 = 6272 units in magnitude (T = 14 P + Pr at most 15 * 6272), far
+//     below 2^24, so the fp32 MFMA result is the exact integer sum times 2^-18;
+//   * the block rows' CSR lists of chosen residual blocks are walked in step with
+//     g (the "zipper"); a chosen 64-wide block costs one more MFMA per output
+//     tile on the same activation operands, giving Pr exactly;
+//   * each group is dequantized into an fp32 accumulator: acc += s * 2^18 * P,
+//     and for a group with chosen blocks acc += fp32(s / 14) * 2^18 * (14 P + Pr)
+//     (decode kernel) or acc += s * 2^18 * P + fp32(s / 14) * 2^18 * Pr (prefill);
+//   * the epilogue multiplies by the token scale sx and stores bf16 (RNE) or fp32.
+// The debug build (acc_dump) writes every group's exact T = 14 P + Pr.
 #include <algorithm>
 #include <cmath>
 
@@ -25,20 +30,6 @@
 #include "mq_internal.h"
 
 namespace mq {
-
-// The zipper: CSR positions of the residual blocks of one block row, for the
-// column blocks a wave walks, gathered into an LDS table in one parallel pass
-// (lane i reads list entry lo + i), so the K loop finds each group's blocks
-// with an LDS read instead of a chain of dependent loads.
-__device__ __forceinline__ void zip_table(const GemmArgs& a, int br, int kb0, int nkb, int* tab,
-                                          int lane, int nlanes) {
-    const int lo = clampi(a.row_ptr[br], 0, a.nnz);
-    const int hi = clampi(a.row_ptr[br + 1], lo, a.nnz);
-    for (int i = lo + lane; i < hi; i += nlanes) {
-        const int rel = a.col_idx[i] - kb0;
-        if (rel >= 0 && rel < nkb) tab[rel] = i;
-    }
-}
 
 __device__ __forceinline__ void store_out(const GemmArgs& a, int OUTMODE, int m, int n, float v) {
     const int64_t idx = static_cast<int64_t>(m) * a.N + n;
@@ -211,8 +202,11 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
 
-    const int lo = RES ? clampi(a.row_ptr[br], 0, a.nnz) : 0;
-    const int hi = RES ? clampi(a.row_ptr[br + 1], lo, a.nnz) : 0;
+    // block positions come from the dense block map when there is one (then the
+    // payload is addressed from its start), else from the block row's CSR list
+    const bool map = a.rmap != nullptr;
+    const int lo = RES && !map ? clampi(a.row_ptr[br], 0, a.nnz) : 0;
+    const int hi = RES ? (map ? a.nnz : clampi(a.row_ptr[br + 1], lo, a.nnz)) : 0;
     DecSrc src;
     src.w = buf_rsrc(a.wq + wq_tile(nt, G, 0), static_cast<uint32_t>(G) * 1024u);
     src.x = buf_rsrc(a.xq, static_cast<uint32_t>(a.M) * static_cast<uint32_t>(a.K / 2));
@@ -234,14 +228,25 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
         // wave alone while its first loads are in flight: no workgroup barrier.
         // A wavefront's LDS operations complete in issue order, so the -1 fill,
         // the CSR positions and the later reads need no wait between lanes.
+        // With a block map the table is one coalesced load of the wave's entries
+        // (out-of-range positions read as "no block"); no dependent loads.
         const int kb0 = 2 * gb, kb1 = 2 * ge;
-        for (int i = kb0 + lane; i < kb1; i += 64) tab[i] = -1;
-        __builtin_amdgcn_wave_barrier();
-        for (int i = lo + lane; i < hi; i += 64) {
-            const int kb = a.col_idx[i];
-            if (kb >= kb0 && kb < kb1) tab[kb] = i;
+        for (int i = kb0 + lane; i < kb1; i += 64) {
+            int v = -1;
+            if (map) {
+                v = a.rmap[static_cast<int64_t>(br) * (2 * G) + i];
+                v = (v >= 0 && v < a.nnz) ? v : -1;
+            }
+            tab[i] = v;
         }
         __builtin_amdgcn_wave_barrier();
+        if (!map) {
+            for (int i = lo + lane; i < hi; i += 64) {
+                const int kb = a.col_idx[i];
+                if (kb >= kb0 && kb < kb1) tab[kb] = i;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
         if (gb < ge) dec_fetch_res<MT, QS, RES>(s0, a, src, tab, rrow, G, gb, lane);
     }
     for (int g = gb; g < ge; g += 2 * QS) {
@@ -272,347 +277,11 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
     }
 }
 
-// ===========================================================================
-// Prefill kernel, M > 32: 128 x 128 output tile per workgroup, four waves of
-// 64 x 64 (2 x 2), one 128-wide K group per step, 32 x 32 x 64 fp8 MFMAs.
-//   * The instruction is 64 inputs deep, so a group is two MFMAs per 32 x 32
-//     tile, one per half, and a chosen 64-wide residual block (one half of a
-//     group) is exactly one more MFMA per tile: no zero-padded depth.
-//   * Activations are widened once per workgroup: every wave loads 1 KB runs
-//     of the group's activation nibbles (16 rows x 64 bytes, lane 16 kc + r
-//     holds row r, bytes 16 kc .. 16 kc + 15), turns them into fp8 operand
-//     bytes and stores them in LDS in MFMA lane order, so each operand read is
-//     two conflict-free 1 KB LDS reads shared by the two waves of its rows.
-//   * Weights go straight from memory into registers (each wave owns its 64
-//     columns; the other wave that uses them finds them in L2), one group
-//     ahead, and are widened per wave right before their MFMAs.
-//   * Per group: exact products P (and Pr) of each 32 x 32 tile, then
-//     acc += fp32(s) * 2^18 * P, and acc += fp32(s / 14) * 2^18 * Pr for a
-//     half holding a chosen block of the wave's block row (a scalar branch:
-//     a wave's 64 columns lie in one block row).
-//   * One barrier per group: the next group's activations are written to the
-//     other LDS stage after this group's MFMAs; global loads are waited on by
-//     count (their registers are not read until a group later).
-// 32 x 32 MFMA layouts: operand lane l holds row (A) / column (B) l % 32 and
-// the inputs of K half l / 32; result register r of lane l is row
-// 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
-// ===========================================================================
-constexpr int kPM = 128, kPN = 128;
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ v16f mfma32_f8(v8i a, v8i b, v16f c) {
     // format selectors 0/0 (e4m3 both operands), no block scales
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
-// One prefill step's register-resident loads (a group ahead of its use).
-struct PfLoads {
-    uint4 b[2][2];     // weight nibbles [column tile j][half h]
-    uint4 x[2];        // activation nibbles for the LDS fill (two 1 KB runs per wave)
-};
-
-// A group's residual codes of its first chosen half [column tile j] (zero where no
-// block is chosen); when both halves hold chosen blocks (rare at these budgets),
-// the second half's codes are fetched where they are used.
-struct PfRes {
-    uint4 r[2];
-    int rmask;         // bit h: half h of the group holds a chosen block (wave-uniform)
-    int jb1;           // CSR position of half 1's block, or -1
-};
-
-template <bool RES, bool DUMP, int OUTMODE>
-__global__ __launch_bounds__(256, DUMP ? 1 : 2) void k_gemm_prefill(GemmArgs a) {
-    // activation operands in fp8: two stages of two groups each,
-    // [stage][group slot][M tile 4][half 2][part 2][lane 64][16 B]
-    __shared__ __align__(16) uint8_t xs[2][2][4][2][2][1024];
-    __shared__ int tab[RES ? 2 * 2 * kMaxGroups : 1];                // [2 block rows][2G]
-    // the wave index is uniform in a wave: say so, so that per-wave buffer
-    // resources live in scalar registers (no per-lane waterfall around each load)
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lc = lane & 31, lh = lane >> 5;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int tiles_n = (a.N + kPN - 1) / kPN;
-    const int m0 = (blockIdx.x / tiles_n) * kPM, n0 = (blockIdx.x % tiles_n) * kPN;
-    const int G = a.K / kGroup, G4 = (G + 3) / 4, nbc = 2 * G;
-    const int br0 = n0 / a.bn;
-    const int wc0 = n0 + wn * 64;                                    // this wave's first column
-
-    // zipper tables of the tile's block rows (one or two), gathered once
-    if (RES) {
-        for (int i = tid; i < 2 * nbc; i += 256) tab[i] = -1;
-        __syncthreads();
-        zip_table(a, br0, 0, nbc, tab, tid, 256);
-        if ((n0 + kPN - 1) / a.bn != br0 && n0 + 64 < a.N) zip_table(a, br0 + 1, 0, nbc, tab + nbc, tid, 256);
-        __syncthreads();
-    }
-
-    // weights of this wave's 64 columns: four 16-row tiles; tiles past N read zero
-    const int wtiles = max(0, min(4, (a.N - wc0) / 16));
-    const __amdgpu_buffer_rsrc_t rb =
-        buf_rsrc_uniform(a.wq + static_cast<int64_t>(wc0 >> 4) * G * 1024, static_cast<uint32_t>(wtiles) * G * 1024u);
-    // lane's offset for column tile j, half h (group 0): tile 2j + lc/16, row lc%16, chunk 2h + lh
-    uint32_t boff[2][2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-            boff[j][h] = static_cast<uint32_t>(2 * j + (lc >> 4)) * G * 1024u +
-                         static_cast<uint32_t>(((2 * h + lh) * 16 + (lc & 15)) * 16);
-    // the lane's column scales, four groups per 8-byte load (per column tile j)
-    const __amdgpu_buffer_rsrc_t rs =
-        buf_rsrc_uniform(a.sw + static_cast<int64_t>(wc0 >> 4) * G4 * 64, static_cast<uint32_t>(wtiles) * G4 * 128u);
-    uint32_t soff[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-        soff[j] = (static_cast<uint32_t>(2 * j + (lc >> 4)) * G4 * 64u + (lc & 15) * 4u) * 2u;
-
-    // residual payload of this wave's block row, and the lane's rows in it
-    __amdgpu_buffer_rsrc_t rr = buf_rsrc_uniform(a.wq, 0u);
-    int wtab = 0, wlo = 0;
-    uint32_t rrow = 0;
-    if (RES && wc0 < a.N) {
-        const int brw = wc0 / a.bn;
-        wtab = (brw - br0) * nbc;
-        wlo = clampi(a.row_ptr[brw], 0, a.nnz);
-        const int whi = clampi(a.row_ptr[brw + 1], wlo, a.nnz);
-        rr = buf_rsrc_uniform(whi > wlo ? a.rq + static_cast<int64_t>(wlo) * a.bn * 32 : a.wq,
-                      static_cast<uint32_t>(whi - wlo) * static_cast<uint32_t>(a.bn) * 32u);
-        rrow = static_cast<uint32_t>(wc0 % a.bn + lc);
-    }
-
-    // activation fill: this wave's two 1 KB runs of a group (rows 32 wave + 16 u + lane % 16)
-    const uint32_t x_range = static_cast<uint32_t>(max(0, min(a.M - m0, kPM))) * 64u;
-    uint32_t xoff[2];
-    int xdst[2][2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int row = 32 * wave + 16 * u + (lane & 15), kc = lane >> 4;
-        xoff[u] = static_cast<uint32_t>(row) * 64u + kc * 16u;
-        const int lp = (row & 31) + 32 * (kc & 1);
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-            xdst[u][p] = ((((row >> 5) * 2 + (kc >> 1)) * 2 + p) * 64 + lp) * 16;
-    }
-
-    // Loads of the steady state are issued unconditionally (a group index past the
-    // end is clamped to the last group, an absent residual half reads past its
-    // buffer's range and returns zeros), so the compiler counts outstanding loads
-    // exactly and waits only for the data it uses.
-    auto load_x = [&](int g, PfLoads& L) {
-        const int gc = min(g, G - 1);
-        const __amdgpu_buffer_rsrc_t rx = buf_rsrc_uniform(a.xq + (static_cast<int64_t>(gc) * a.M + m0) * 64, x_range);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) L.x[u] = buf_load16(rx, xoff[u]);
-    };
-    auto load_w = [&](int g, PfLoads& L) {
-        const uint32_t gc = static_cast<uint32_t>(min(g, G - 1));
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) L.b[j][h] = buf_load16(rb, boff[j][h] + gc * 1024u);
-    };
-    // the group's residual codes, fetched at the start of the step that uses them
-    // (before the next group's weights, so waiting for them does not wait for those)
-    auto res_off = [&](int jb, int j) {
-        return jb >= 0 ? ((jb - wlo) * static_cast<uint32_t>(a.bn) + rrow + 32u * j) * 32u + lh * 16u : 0x80000000u;
-    };
-    auto load_res = [&](int g, PfRes& R) {
-        const int jb0 = __builtin_amdgcn_readfirstlane(tab[wtab + 2 * g]);
-        const int jb1 = __builtin_amdgcn_readfirstlane(tab[wtab + 2 * g + 1]);
-        R.rmask = (jb0 >= 0 ? 1 : 0) | (jb1 >= 0 ? 2 : 0);
-        R.jb1 = jb1;
-        const int jb = jb0 >= 0 ? jb0 : jb1;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) R.r[j] = buf_load16(rr, res_off(jb, j));
-    };
-    // widen the loaded activation runs into stage st of the LDS operands
-    auto store_x = [&](const PfLoads& L, int st, int slot) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const v8i v = f8_operand(L.x[u]);
-            *reinterpret_cast<v4i*>(&xs[st][slot][0][0][0][0] + xdst[u][0]) = v4i{v[0], v[1], v[2], v[3]};
-            *reinterpret_cast<v4i*>(&xs[st][slot][0][0][0][0] + xdst[u][1]) = v4i{v[4], v[5], v[6], v[7]};
-        }
-    };
-    // the lane's fp16 scales of the current and the next quad of groups, per column tile
-    uint2 sc[2], scn[2];
-    auto load_scales = [&](int q, uint2 (&dst)[2]) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) dst[j] = buf_load8(rs, soff[j] + static_cast<uint32_t>(q) * 128u);
-    };
-
-
-    v16f acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    // debug build: the exact group sums, 14 P from the base pass, plus Pr from the
-    // residual pass (each entry is owned by one lane, so the update needs no atomics)
-    auto dump_idx = [&](int i, int j, int r, int g) -> int64_t {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        const int nn = wc0 + j * 32 + lc;
-        return (m < a.M && nn < a.N) ? (static_cast<int64_t>(m) * a.N + nn) * G + g : -1;
-    };
-    auto a_operand = [&](int st, int i, int h) {
-        const uint8_t* base = &xs[st >> 1][st & 1][wm * 2 + i][h][0][0];
-        const v4i lo = *reinterpret_cast<const v4i*>(base + lane * 16);
-        const v4i hi = *reinterpret_cast<const v4i*>(base + 1024 + lane * 16);
-        return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-
-    // one group g (u = g % 4, a constant at every call site, so the scale word and
-    // half are picked without an index): operands of stage st, weights of L,
-    // residual codes of R, scales sc
-    auto compute = [&](int g, int u, int st, const PfLoads& L, const PfRes& R) {
-        float sv[2], fs[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t w2 = (u & 2) ? sc[j].y : sc[j].x;
-            sv[j] = f16_bits_to_f32(static_cast<uint16_t>(w2 >> (16 * (u & 1))));
-            fs[j] = sv[j] * kF8Unit;
-        }
-        // base pass: every group, acc += s * P
-        v8i bop[2][2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) bop[j][h] = f8_operand(L.b[j][h]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const v8i a0 = a_operand(st, i, 0), a1 = a_operand(st, i, 1);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const v16f z = {};
-                v16f p = mfma32_f8(a0, bop[j][0], z);
-                p = mfma32_f8(a1, bop[j][1], p);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(fs[j], p[r], acc[i][j][r]);
-                if (DUMP) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int64_t d = dump_idx(i, j, r, g);
-                        if (d >= 0) a.acc_dump[d] = 14 * static_cast<int>(p[r] * kF8Unit);
-                    }
-                }
-            }
-        }
-        // residual pass, only in a group whose half (or halves) hold a chosen block
-        // of the wave's block row (a scalar branch): one MFMA per tile and chosen
-        // half on the same LDS activation operands, acc += fp32(s / 14) * Pr
-        const int rmask = RES ? R.rmask : 0;
-        if (RES && rmask) {
-            const int ha = (rmask & 1) ? 0 : 1;         // the half whose codes R holds
-            const bool both = rmask == 3;
-            float fr[2];
-            v8i ra[2], rb2[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                fr[j] = div14(sv[j]) * kF8Unit;
-                ra[j] = f8_operand(R.r[j]);
-            }
-            if (both) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) rb2[j] = f8_operand(buf_load16(rr, res_off(R.jb1, j)));
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const v8i aa = a_operand(st, i, ha);
-                v8i ab;
-                if (both) ab = a_operand(st, i, 1);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const v16f z = {};
-                    v16f pr = mfma32_f8(aa, ra[j], z);
-                    if (both) pr = mfma32_f8(ab, rb2[j], pr);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(fr[j], pr[r], acc[i][j][r]);
-                    if (DUMP) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int64_t d = dump_idx(i, j, r, g);
-                            if (d >= 0) a.acc_dump[d] += static_cast<int>(pr[r] * kF8Unit);
-                        }
-                    }
-                }
-            }
-        }
-    };
-
-    // Pipeline: a stage of LDS holds the activation operands of two consecutive
-    // groups, so one barrier serves two groups. Step g computes group g from
-    // stage (g/2)%2, slot g%2, with its weights in Lc; it stores group g+2's
-    // activations (loaded a step earlier, in Lc.x) into the other stage, and loads
-    // group g+1's weights and group g+3's activations into Ln. The loop is
-    // unrolled by a quad of groups, so the two register sets alternate without
-    // copies and u = g % 4 is a constant.
-    PfLoads L0, L1;
-    load_x(0, L0);
-    load_w(0, L0);
-    load_scales(0, sc);
-    load_scales(min(1, G4 - 1), scn);
-    store_x(L0, 0, 0);
-    load_x(1, L0);
-    store_x(L0, 0, 1);
-    load_x(2, L0);
-    __syncthreads();
-    auto step = [&](int g, int u, PfLoads& Lc, PfLoads& Ln) {
-        PfRes R;
-        R.rmask = 0;
-        if (RES) load_res(g, R);
-        load_w(g + 1, Ln);
-        if (u == 0 && g > 0) {
-            // the prefetched scales become current; the next quad's are loaded
-#pragma unroll
-            for (int j = 0; j < 2; ++j) sc[j] = scn[j];
-            load_scales(min((g >> 2) + 1, G4 - 1), scn);
-        }
-        compute(g, u, ((u >> 1) << 1) | (u & 1), Lc, R);
-        store_x(Lc, ((u >> 1) & 1) ^ 1, u & 1);
-        load_x(g + 3, Ln);
-        if (u & 1) __syncthreads();
-    };
-    for (int g = 0; g < G; g += 4) {
-        step(g, 0, L0, L1);
-        if (g + 1 >= G) break;
-        step(g + 1, 1, L1, L0);
-        if (g + 2 >= G) break;
-        step(g + 2, 2, L0, L1);
-        if (g + 3 >= G) break;
-        step(g + 3, 3, L1, L0);
-    }
-
-    // Epilogue: the lane's 32 token scales are loaded together (rows past M read
-    // zero through the range check), then y = acc * sx is stored as bf16 or fp32.
-    const int mw = m0 + wm * 64;
-    float sxr[2][16];
-    if (OUTMODE == 0) {
-        const __amdgpu_buffer_rsrc_t rsx = buf_rsrc_uniform(a.sx + mw, static_cast<uint32_t>(max(0, min(64, a.M - mw))) * 4u);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                sxr[i][r] = __builtin_bit_cast(float, buf_load4(rsx, static_cast<uint32_t>(i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)) * 4u));
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int nn = wc0 + j * 32 + lc;
-            if (nn >= a.N) continue;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = mw + i * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (m >= a.M) continue;
-                const int64_t idx = static_cast<int64_t>(m) * a.N + nn;
-                if (OUTMODE == 1) a.ws[idx] = acc[i][j][r];
-                else if (a.y_bf16) static_cast<uint16_t*>(a.y)[idx] = f32_to_bf16_bits(acc[i][j][r] * sxr[i][r]);
-                else static_cast<float*>(a.y)[idx] = acc[i][j][r] * sxr[i][r];
-            }
-        }
 }
 
 // Workgroup b of a grid of T runs on XCD b % 8 (the dispatcher deals workgroups
@@ -708,13 +377,21 @@ __global__ __launch_bounds__(64 * NWN, DUMP ? 1 : 2) void k_gemm_wide(GemmArgs a
     const __amdgpu_buffer_rsrc_t rnull = buf_rsrc_uniform(a.wq, 0u);   // reads zeros
     int wlo = 0, rbase = 0;
     if (RES) {
-        for (int i = lane; i < nbc; i += 64) wt[i] = -1;
+        const bool map = a.rmap != nullptr;
+        const int brw = min(wc0, a.N - 1) / a.bn;
+        for (int i = lane; i < nbc; i += 64) {
+            int v = -1;
+            if (map && wc0 < a.N) {
+                v = a.rmap[static_cast<int64_t>(brw) * nbc + i];
+                v = (v >= 0 && v < a.nnz) ? v : -1;
+            }
+            wt[i] = v;
+        }
         __builtin_amdgcn_wave_barrier();
         if (wc0 < a.N) {
-            const int brw = wc0 / a.bn;
-            wlo = clampi(a.row_ptr[brw], 0, a.nnz);
-            const int whi = clampi(a.row_ptr[brw + 1], wlo, a.nnz);
-            for (int i = wlo + lane; i < whi; i += 64) {
+            wlo = map ? 0 : clampi(a.row_ptr[brw], 0, a.nnz);
+            const int whi = map ? a.nnz : clampi(a.row_ptr[brw + 1], wlo, a.nnz);
+            for (int i = map ? whi : wlo + lane; i < whi; i += 64) {
                 const int kb = a.col_idx[i];
                 if (kb >= 0 && kb < nbc) wt[kb] = i;
             }
@@ -1035,13 +712,6 @@ template <int MT, bool RES, bool DUMP, int OUT>
 static hipError_t go_decode(const GemmArgs& a, hipStream_t st) {
     const DecodePlan p = plan_decode(a.M, a.N, a.K);
     k_gemm_decode<MT, RES, DUMP, OUT><<<dim3(a.N / 16), dim3(64 * p.nw), 0, st>>>(a);
-    return hipGetLastError();
-}
-
-template <bool RES, bool DUMP, int OUT>
-static hipError_t go_prefill(const GemmArgs& a, hipStream_t st) {
-    const int tiles = ((a.M + kPM - 1) / kPM) * ((a.N + kPN - 1) / kPN);
-    k_gemm_prefill<RES, DUMP, OUT><<<dim3(tiles), dim3(256), 0, st>>>(a);
     return hipGetLastError();
 }
 

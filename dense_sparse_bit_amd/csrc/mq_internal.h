@@ -13,6 +13,7 @@ struct GemmArgs {
     const uint16_t* sw;
     const int32_t* row_ptr;
     const int32_t* col_idx;
+    const int32_t* rmap;       // dense block map [N/bn][K/64] (CSR position or -1), or null
     const uint8_t* rq;
     int nnz;
     int M, N, K, bn;
@@ -52,6 +53,8 @@ hipError_t launch_select(const float* w, const float* h, int64_t N, int64_t K, i
 hipError_t launch_pack(const float* w, int64_t N, int64_t K, int bn, const int32_t* row_ptr,
                        const int32_t* col_idx, int64_t nnz, uint8_t* wq, uint16_t* sw, uint8_t* rq,
                        hipStream_t st);
+hipError_t launch_block_map(const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz, int64_t N, int64_t K,
+                            int bn, int32_t* rmap, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, GemmKind kind, hipStream_t st);
 hipError_t launch_residual_merge(const GemmArgs& a, hipStream_t st);
 

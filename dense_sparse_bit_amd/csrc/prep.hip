@@ -567,6 +567,32 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// The dense block map of a CSR selection: one workgroup per block row writes -1
+// over the row, then each CSR entry p of the row writes p at its column block.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_block_map(const int32_t* __restrict__ row_ptr,
+                                                   const int32_t* __restrict__ col_idx, int nnz, int nkb,
+                                                   int32_t* __restrict__ rmap) {
+    const int br = blockIdx.x;
+    int32_t* row = rmap + static_cast<int64_t>(br) * nkb;
+    for (int i = threadIdx.x; i < nkb; i += blockDim.x) row[i] = -1;
+    __syncthreads();
+    const int lo = min(max(row_ptr[br], 0), nnz);
+    const int hi = min(max(row_ptr[br + 1], lo), nnz);
+    for (int p = lo + static_cast<int>(threadIdx.x); p < hi; p += blockDim.x) {
+        const int kb = col_idx[p];
+        if (kb >= 0 && kb < nkb) row[kb] = p;
+    }
+}
+
+hipError_t launch_block_map(const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz, int64_t N, int64_t K,
+                            int bn, int32_t* rmap, hipStream_t st) {
+    k_block_map<<<dim3(static_cast<unsigned>(N / bn)), dim3(256), 0, st>>>(row_ptr, col_idx, static_cast<int>(nnz),
+                                                                          static_cast<int>(K / kBk), rmap);
+    return hipGetLastError();
+}
+
 hipError_t launch_hessian(const void* x, int bf16, int64_t M, int64_t K, const float* colscale, float* h,
                           hipStream_t st) {
     const int64_t blocks = (K + kHCh - 1) / kHCh;

@@ -209,6 +209,32 @@ int mq_gemm_w4a4_residual(const uint8_t* xq, const float* sx, const uint8_t* wq,
                           void* stream);
 
 /*
+ * The dense block map of a selection (Methodology 3: the fused kernel finds each
+ * 128-group's residual blocks in step with the K loop; with the map that lookup is
+ * one coalesced load per wavefront instead of a walk of the block row's list):
+ *   rmap[b][j] = p  if col_idx[p] == j for some p in [row_ptr[b], row_ptr[b+1]),
+ *              = -1 otherwise,
+ * for block rows b < N/bn and column blocks j < K/bk. rmap: int32 [N/bn][K/bk]
+ * (device, 4-byte aligned), fully overwritten. Entries with a column-block index
+ * outside [0, K/bk) are skipped; for a block listed twice in one row, one of its
+ * positions is kept. Row pointers are clamped to [0, nnz]. Asynchronous.
+ */
+int mq_block_map(const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz, int64_t N, int64_t K,
+                 int bn, int bk, int32_t* rmap, void* stream);
+
+/*
+ * mq_gemm_w4a4_residual with the chosen blocks found through a block map
+ * (mq_block_map of the CSR lists the payload was packed with) instead of the lists:
+ * the same kernels and the same arithmetic, so y and acc_dump are bit-identical to
+ * mq_gemm_w4a4_residual's. Map entries outside [0, nnz) mean "no block".
+ * Requires nnz * bn * bk / 2 <= 2^31 (else MQ_ERR_UNSUPPORTED).
+ */
+int mq_gemm_w4a4_residual_mapped(const uint8_t* xq, const float* sx, const uint8_t* wq,
+                                 const uint16_t* sw, const int32_t* rmap, const uint8_t* rq,
+                                 int64_t nnz, int64_t M, int64_t N, int64_t K, int group, int bn,
+                                 int bk, void* y, int y_dtype, int32_t* acc_dump, void* stream);
+
+/*
  * Dense-only 4-bit GEMM: the same kernel with the residual path compiled out
  * (the "dense 4-bit GEMM kernel" the residual is fused into, Methodology 3).
  * y = sx * sum_g s * P. With nnz == 0 the fused call gives the same bits.

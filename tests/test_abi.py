@@ -34,7 +34,7 @@ def mq():
 def test_header_declares_the_boundary():
     names = _declared()
     for fn in ["mq_quantize_act", "mq_pack_weights", "mq_select_blocks", "mq_gemm_w4a4_residual",
-               "mq_select_workspace_bytes",
+               "mq_select_workspace_bytes", "mq_block_map", "mq_gemm_w4a4_residual_mapped",
                "mq_hessian_diag", "mq_gemm_w4a4_dense", "mq_gemm_residual_separate",
                "mq_status_string", "mq_version"]:
         assert fn in names
@@ -125,6 +125,22 @@ def test_preparation_calls_reject_bad_arguments(lib_nogpu):
                                         None) == -1
     # the packed activation layout is group-major, so K must be a multiple of 128
     assert lib.mq_quantize_act(FAKE, 1, 4, 130, FAKE, FAKE, None) == -2
+    # block map: outputs and lists are checked, shapes as for the other calls
+    assert lib.mq_block_map(FAKE, FAKE, 3, 512, 512, 64, 64, None, None) == -1
+    assert lib.mq_block_map(None, FAKE, 3, 512, 512, 64, 64, FAKE, None) == -1
+    assert lib.mq_block_map(FAKE, None, 3, 512, 512, 64, 64, FAKE, None) == -1
+    assert lib.mq_block_map(FAKE, FAKE, nb + 1, 512, 512, 64, 64, FAKE, None) == -1
+    assert lib.mq_block_map(FAKE, FAKE, 3, 512, 500, 64, 64, FAKE, None) == -2
+    # the mapped GEMM needs a map, a 16-byte aligned payload, and 32-bit payload offsets
+    mapped = lambda **kw: lib.mq_gemm_w4a4_residual_mapped(
+        FAKE, FAKE, FAKE, FAKE, kw.get("rmap", FAKE), kw.get("rq", FAKE), kw.get("nnz", 3), 4,
+        kw.get("N", 512), kw.get("K", 512), 128, kw.get("bn", 64), 64, FAKE, 1, None, None)
+    assert mapped(rmap=None) == -1
+    assert mapped(rq=None) == -1
+    assert mapped(rq=FAKE + 4) == -1
+    assert mapped(nnz=nb + 1) == -1
+    assert mapped(K=320) == -2
+    assert mapped(N=1 << 17, K=65536, bn=128, nnz=(1 << 31) // (128 * 32) + 1) == -2
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -154,6 +154,25 @@ def _check(mq, orc, inp, k_blocks, out_dtype_name="bf16", rows=None, check_varia
     say(f"[parity] {cfg.name} y max rel err {err_p:.3e} (production build)")
     assert err_p <= Y_TOL[out_dtype_name]
     assert torch.equal(bits(yp), bits(g["y"])), "production and debug builds differ"
+    # the block map of the selection, and the same GEMM finding its blocks through it:
+    # the map is the oracle's CSR scattered into a dense table; y and the group sums
+    # are the list-walking call's bits
+    rmap = mq.block_map(g["row_ptr"], g["col_idx"], cfg.N, cfg.K, bn=cfg.bn)
+    exp = np.full((cfg.N // cfg.bn, cfg.K // cfg.bk), -1, dtype=np.int32)
+    for b in range(cfg.N // cfg.bn):
+        for p in range(ref["row_ptr"][b], ref["row_ptr"][b + 1]):
+            exp[b, ref["col_idx"][p]] = p
+    np.testing.assert_array_equal(_np(rmap), exp)
+    ym = mq.gemm_w4a4_residual(g["xq"], g["sx"], g["wq"], g["sw"], g["row_ptr"], g["col_idx"], g["rq"],
+                               cfg.K, bn=cfg.bn, out_dtype=out_dtype, rmap=rmap)
+    mdump = torch.empty_like(g["dump"])
+    ymd = mq.gemm_w4a4_residual(g["xq"], g["sx"], g["wq"], g["sw"], g["row_ptr"], g["col_idx"], g["rq"],
+                                cfg.K, bn=cfg.bn, out_dtype=out_dtype, rmap=rmap, acc_dump=mdump)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(ym), bits(yp)), "the mapped call differs from the list-walking call"
+    assert torch.equal(bits(ymd), bits(yp))
+    md = mdump[sel] if rows is None else mdump[torch.as_tensor(rows, device="cuda")]
+    np.testing.assert_array_equal(_np(md).astype(np.int64), ref["T"])
     if check_variants:
         # dense-only kernel: T = 14 P, and y equals the fused kernel with no residual
         ddump = torch.empty_like(g["dump"])
