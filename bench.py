@@ -166,14 +166,35 @@ def bench_variants(mq, torch, layer, k_blocks, calls, bf16=True):
         mq.gemm_residual_separate(xq, sx, s["wq"], s["sw"], s["row_ptr"], s["col_idx"], s["rq"], K,
                                   bn=bn, y=y, ws=wsb)
 
+    # the per-call path from unquantized activations: quantize_act then the fused
+    # GEMM (two launches), against the GEMM that quantizes its own activations
+    xq2, sx2 = torch.empty_like(xq), torch.empty_like(sx)
+    sync = mq.sync_words()
+
+    def quant_then_fused(i):
+        s = sets[i % n]
+        mq.quantize_act(layer.x, xq=xq2, sx=sx2)
+        mq.gemm_w4a4_residual(xq2, sx2, s["wq"], s["sw"], s["row_ptr"], s["col_idx"], s["rq"], K, bn=bn, y=y,
+                              rmap=s["rmap"])
+
+    def fused_act(i, launch="auto"):
+        s = sets[i % n]
+        mq.gemm_w4a4_residual_act(layer.x, s["wq"], s["sw"], s["rmap"], s["rq"], K, bn=bn, y=y, xq=xq2, sx=sx2,
+                                  sync=sync, launch=launch)
+
+    legs = [("dense", dense), ("fused", fused), ("fused_csr", fused_csr), ("separate", separate),
+            ("quant_then_fused", quant_then_fused), ("fused_act", fused_act)]
+    if cfg.M <= 32:
+        legs.append(("fused_act_one", lambda i: fused_act(i, "one")))
     out = {}
-    for name, fn in (("dense", dense), ("fused", fused), ("fused_csr", fused_csr), ("separate", separate)):
+    for name, fn in legs:
         fn(calls - 1)
         torch.cuda.synchronize()
         y_eager = y.clone()
         out[name] = _graph_time_us(torch, fn, calls)
         if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
             raise RuntimeError(f"graph replay of the {name} GEMM differs from the eager call")
+    out["act_auto_one"] = 1.0 if mq.act_one_launch(cfg.M, cfg.N, cfg.K) else 0.0
     del sets
     if bf16:
         # the W16A16 context: the same layer as a bf16 matmul (hipBLASLt), weights rotated too
@@ -207,6 +228,15 @@ def leg_record(cfg, pct, k_blocks, t):
            "overhead_vs_dense": round(t["fused"] / t["dense"] - 1, 4),
            "overhead_csr_vs_dense": round(t["fused_csr"] / t["dense"] - 1, 4),
            "separate_overhead_vs_dense": round(t["separate"] / t["dense"] - 1, 4)}
+    if "fused_act" in t:
+        # from unquantized activations: quantize_act + the GEMM (two launches), the
+        # self-quantizing call as its "auto" rule runs it, and forced to one launch
+        rec["quant_then_fused_us"] = round(t["quant_then_fused"], 3)
+        rec["act_auto_us"] = round(t["fused_act"], 3)
+        rec["act_auto_form"] = "one" if t["act_auto_one"] else "two"
+        if "fused_act_one" in t:
+            rec["act_one_launch_us"] = round(t["fused_act_one"], 3)
+            rec["act_one_launch_saving"] = round(1 - t["fused_act_one"] / t["quant_then_fused"], 4)
     if "bf16_matmul" in t:
         rec["bf16_matmul_us"] = round(t["bf16_matmul"], 3)
         rec["speedup_fused_vs_bf16"] = round(t["bf16_matmul"] / t["fused"], 3)
@@ -621,7 +651,9 @@ def main():
                 legs.append(rec)
                 log(f"[bench] leg {c.name} {b}%: fused {tb['fused']:.2f} dense {tb['dense']:.2f} "
                     f"separate {tb['separate']:.2f} us, overhead {rec['overhead_vs_dense']:.3f}, "
-                    f"{rec['fused']['hbm_frac']:.3f} of 8 TB/s")
+                    f"{rec['fused']['hbm_frac']:.3f} of 8 TB/s; quantize+fused {tb['quant_then_fused']:.2f}, "
+                    f"self-quantizing one launch {tb.get('fused_act_one', float('nan')):.2f}, "
+                    f"auto ({rec['act_auto_form']}) {tb['fused_act']:.2f} us")
             del lay
             torch.cuda.empty_cache()
 

@@ -44,6 +44,8 @@ _SIGS = {
                               _p, _int, _p, _p],
     "mq_gemm_w4a4_dense": [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p, _int, _p, _p],
     "mq_block_map": [_p, _p, _i64, _i64, _i64, _int, _int, _p, _p],
+    "mq_gemm_w4a4_residual_act": [_p, _int, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
+                                  _p, _p, _p, _int, _p, _int, _p],
     "mq_gemm_w4a4_residual_mapped": [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
                                      _p, _int, _p, _p],
     "mq_gemm_residual_separate": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int,
@@ -412,6 +414,63 @@ def gemm_w4a4_residual(xq, sx, wq, sw, row_ptr, col_idx, rq, K: int, bn: int = 6
           _ptr(col_idx) if nnz else None, _ptr(rq) if nnz else None, nnz, M, N, K, GROUP, bn, BK,
           _ptr(y), _y_dtype(y.dtype), _ptr(acc_dump), _stream(stream))
     return y
+
+
+SYNC_WORDS = 544   # MQ_SYNC_WORDS
+
+
+def sync_words(device="cuda"):
+    """The zero-filled int32 [SYNC_WORDS] counter array gemm_w4a4_residual_act needs (one per
+    stream of calls; every completed call leaves it zero again)."""
+    return torch.zeros(SYNC_WORDS, dtype=torch.int32, device=device)
+
+
+_ACT_LAUNCH = {"auto": 0, "one": 1, "two": 2}   # MQ_ACT_AUTO, MQ_ACT_ONE_LAUNCH, MQ_ACT_TWO_LAUNCHES
+
+
+def act_one_launch(M: int, N: int, K: int, launch: str = "auto") -> bool:
+    """Whether gemm_w4a4_residual_act runs as one launch (the library's own rule for
+    "auto": M <= 32 and M N <= 8 K)."""
+    return launch == "one" or (launch == "auto" and M <= 32 and M * N <= 8 * K)
+
+
+def gemm_w4a4_residual_act(x, wq, sw, rmap, rq, K: int, bn: int = 64, out_dtype=torch.bfloat16, y=None,
+                           xq=None, sx=None, sync=None, launch: str = "auto", stream=None):
+    """The fused GEMM that quantizes its own activations: x fp32/bf16 [M][K] in,
+    y out, plus the codes and scales it used (xq, sx, as quantize_act writes them).
+    Returns (y, xq, sx). launch: "one" (M <= 32), "two" (quantize_act, then the
+    GEMM) or "auto"; sync: sync_words(), required when one launch runs."""
+    if launch not in _ACT_LAUNCH:
+        raise ValueError(f"launch must be one of {sorted(_ACT_LAUNCH)}, got {launch!r}")
+    M, K2 = _shape2(x, "x")
+    if K2 != K:
+        raise ValueError(f"x has {K2} inputs, expected K = {K}")
+    _x_dtype(x)
+    _device_contig(x, "x")
+    if xq is None:
+        xq = torch.empty((K // GROUP, M, 64), dtype=torch.uint8, device=x.device)
+    if sx is None:
+        sx = torch.empty(M, dtype=torch.float32, device=x.device)
+    _buf(sx, "sx", 4 * M, _F32)
+    M2, N = _gemm_operands(xq, sx, wq, sw, K)
+    nnz = int(rq.shape[0]) if rq is not None and rq.dim() == 3 else 0
+    _buf(rmap, "rmap", 4 * (N // bn) * (K // BK), _I32)
+    if nnz:
+        _buf(rq, "rq", nnz * bn * BK // 2, _U8, 16)
+    y = _out_checks(y, M, N, out_dtype, wq.device)
+    if launch == "one" and M > 32:
+        raise ValueError("one launch takes at most 32 tokens")
+    one = act_one_launch(M, N, K, launch)
+    if one:
+        if sync is None:
+            raise ValueError("sync (sync_words()) is required for the one-launch form")
+        _buf(sync, "sync", 4 * SYNC_WORDS, _I32, 4)
+    _on_device(x=x, xq=xq, sx=sx, wq=wq, sw=sw, rmap=rmap, rq=rq if nnz else None, y=y,
+               sync=sync if one else None)
+    _call("mq_gemm_w4a4_residual_act", _ptr(x), _x_dtype(x), _ptr(wq), _ptr(sw), _ptr(rmap),
+          _ptr(rq) if nnz else None, nnz, M, N, K, GROUP, bn, BK, _ptr(xq), _ptr(sx),
+          _ptr(sync) if one else None, _ACT_LAUNCH[launch], _ptr(y), _y_dtype(y.dtype), _stream(stream))
+    return y, xq, sx
 
 
 def gemm_w4a4_dense(xq, sx, wq, sw, K: int, out_dtype=torch.bfloat16, y=None, acc_dump=None,

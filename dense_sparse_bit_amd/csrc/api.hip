@@ -79,6 +79,11 @@ mq::GemmArgs make_args(const uint8_t* xq, const float* sx, const uint8_t* wq, co
     a.y_bf16 = y_dtype == MQ_BF16;
     a.acc_dump = acc_dump;
     a.ws = ws;
+    a.x = nullptr;
+    a.x_bf16 = 0;
+    a.xq_w = nullptr;
+    a.sx_w = nullptr;
+    a.sync = nullptr;
     return a;
 }
 
@@ -258,6 +263,47 @@ int mq_gemm_w4a4_residual_mapped(const uint8_t* xq, const float* sx, const uint8
                                nullptr);
     a.rmap = rmap;
     return hip_status(mq::launch_gemm(a, mq::GemmKind::Fused, static_cast<hipStream_t>(stream)));
+}
+
+static_assert(mq::kSyncWords == MQ_SYNC_WORDS, "sync array size");
+
+int mq_gemm_w4a4_residual_act(const void* x, int x_dtype, const uint8_t* wq, const uint16_t* sw,
+                              const int32_t* rmap, const uint8_t* rq, int64_t nnz, int64_t M, int64_t N,
+                              int64_t K, int group, int bn, int bk, uint8_t* xq, float* sx, int32_t* sync,
+                              int launch, void* y, int y_dtype, void* stream) {
+    if (bad_dtype(x_dtype)) return MQ_ERR_INVALID_ARG;
+    if (launch != MQ_ACT_AUTO && launch != MQ_ACT_ONE_LAUNCH && launch != MQ_ACT_TWO_LAUNCHES)
+        return MQ_ERR_INVALID_ARG;
+    int rc = check_gemm(xq, sx, wq, sw, M, N, K, group, bn, bk, y, y_dtype);
+    if (rc) return rc;
+    if (nnz < 0 || nnz > (N / bn) * (K / bk) || !rmap || (nnz > 0 && (!rq || !aligned16(rq))))
+        return MQ_ERR_INVALID_ARG;
+    if (nnz * bn * (bk / 2) > (int64_t(1) << 31)) return MQ_ERR_UNSUPPORTED;
+    if (launch == MQ_ACT_ONE_LAUNCH && M > 32) return MQ_ERR_INVALID_ARG;
+    // measured crossover on MI355X: the one-launch form's wait grows with the
+    // tokens and the column workgroups (M N), the stand-alone quantization with the
+    // row length (K); one launch measured faster up to M N / K = 6.4 and slower
+    // from 9.1 on, so the rule splits at 8
+    const bool one = launch == MQ_ACT_ONE_LAUNCH || (launch == MQ_ACT_AUTO && M <= 32 && M * N <= 8 * K);
+    if (M == 0) return MQ_OK;
+    if (!x || !aligned16(x) || (one && (!sync || (reinterpret_cast<uintptr_t>(sync) & 3u))))
+        return MQ_ERR_INVALID_ARG;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    mq::GemmArgs a = make_args(xq, sx, wq, sw, nullptr, nullptr, rq, nnz, M, N, K, bn, y, y_dtype, nullptr,
+                               nullptr);
+    a.rmap = rmap;
+    if (!one) {
+        // quantization with its own launch (one workgroup per token), then the GEMM
+        hipError_t e = mq::launch_quant_act(x, x_dtype == MQ_BF16, M, K, nullptr, xq, sx, st);
+        if (e == hipSuccess) e = mq::launch_gemm(a, mq::GemmKind::Fused, st);
+        return hip_status(e);
+    }
+    a.x = x;
+    a.x_bf16 = x_dtype == MQ_BF16;
+    a.xq_w = xq;
+    a.sx_w = sx;
+    a.sync = sync;
+    return hip_status(mq::launch_gemm(a, mq::GemmKind::FusedQuantAct, st));
 }
 
 int mq_gemm_w4a4_dense(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint16_t* sw,

@@ -28,6 +28,7 @@
 
 #include "mq_device.h"
 #include "mq_internal.h"
+#include "mq_quant.h"
 
 namespace mq {
 
@@ -78,13 +79,24 @@ struct DecSrc {
 // base tiles, activations and scales of the step starting at group g0 (groups
 // past the last read zero through the range check)
 template <int MT, int QS>
+__device__ __forceinline__ void dec_fetch_x(DecStep<MT, QS>& st, const DecSrc& src, int g0) {
+#pragma unroll
+    for (int u = 0; u < QS; ++u)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) st.x[t][u] = buf_load16(src.x, (g0 + u) * src.xstride + src.xrow[t]);
+}
+
+// X = false leaves the activations to a later dec_fetch_x
+template <int MT, int QS, bool X = true>
 __device__ __forceinline__ void dec_fetch_main(DecStep<MT, QS>& st, const DecSrc& src, int g0, int lane) {
 #pragma unroll
     for (int u = 0; u < QS; ++u) {
         const uint32_t g = g0 + u;
         st.w[u] = buf_load16(src.w, g * 1024u + lane * 16u);
+        if (X) {
 #pragma unroll
-        for (int t = 0; t < MT; ++t) st.x[t][u] = buf_load16(src.x, g * src.xstride + src.xrow[t]);
+            for (int t = 0; t < MT; ++t) st.x[t][u] = buf_load16(src.x, g * src.xstride + src.xrow[t]);
+        }
     }
     const uint32_t so = (g0 >> 2) * 128u + (lane & 15) * 8u + (g0 & 3) * 2u;
     if (QS == 4) {
@@ -183,7 +195,60 @@ __device__ __forceinline__ void dec_compute(const DecStep<MT, QS>& st, const Gem
     }
 }
 
-template <int MT, bool RES, bool DUMP, int OUTMODE>
+// The variant that quantizes its own activations (QX): the first M workgroups each
+// quantize one token (the same arithmetic as the stand-alone kernel) into xq / sx
+// and then count themselves done; the column workgroups wait for that count
+// before their first activation load (their first weights, scales, residual rows
+// and zipper table are already on the way). Workgroups are dispatched in index
+// order, so the quantizing ones always start first and finish without waiting on
+// anything: the wait ends. (It is also bounded: after well under a few seconds a
+// flag is raised in sync[2] and the workgroup goes on.)
+// Each XCD has its own L2, which may hold lines of xq / sx that are not yet
+// current, so a reader must acquire at device scope; that acquire invalidates the
+// whole L2 of its XCD, and one per column workgroup (hundreds per call) costs more
+// than the GEMM. So only the first L = min(16, C) of the C column workgroups
+// (the leaders, dispatched before the rest) take it, once the count is complete;
+// each then raises the ready flag of its own XCD (XCC id from the hardware) and
+// checks in. Any other workgroup goes on once its XCD's flag is up; if every
+// leader has checked in and none ran on its XCD, it takes the acquire itself (so
+// the result does not depend on how workgroups are spread over XCDs). No
+// workgroup of the launch loads xq / sx before that point and the launch starts
+// with invalidated L1s, so an L1 can hold of them only bytes its own CU's
+// quantizing workgroup stored (already final), and every other line any CU loads
+// is filled after an invalidation of its L2 that followed the count.
+// Atomics that return a value keep their workgroup resident until memory answers,
+// which under a full HBM queue is microseconds per workgroup, so the column
+// workgroups use none: waits are plain polling loads, and at the end each adds
+// one to a done count (one of 16, each on its own 128-byte line) without waiting
+// for it or for its output stores. The last column workgroup waits for the other
+// C - 1 counts and then resets the counts and flags, so every completed call
+// leaves the words zero. Every workgroup's reads and stores of the words are
+// complete before its done count is sent, so the reset cannot be seen by any of
+// them.
+constexpr int kSpinLimit = 1 << 20;
+constexpr int kSyncLine = 32;      // int32 words per 128-byte line
+constexpr int kSyncSlots = 16;     // XCC ids 0..15; also the number of leaders
+// line 0: [0] quantized tokens, [2] give-up flag, [3] leaders checked in;
+// line 1 + i: slot i's ready flag and done count
+enum { kSyncCount = 0, kSyncGaveUp = 2, kSyncLeaders = 3, kSyncReady = 0, kSyncDone = 1 };
+static_assert(kSyncLine * (1 + kSyncSlots) == kSyncWords, "sync word layout");
+
+__device__ __forceinline__ int* sync_slot(int* sync, int xcc) { return sync + kSyncLine * (1 + xcc); }
+
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0xF70); }   // vmcnt(0)
+
+__device__ __forceinline__ bool spin_until(const int* p, int target, int* gave_up) {
+    for (int it = 0; __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++it) {
+        if (it >= kSpinLimit) {
+            __hip_atomic_store(gave_up, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(8);
+    }
+    return true;
+}
+
+template <int MT, bool RES, bool DUMP, int OUTMODE, bool QX = false>
 __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a) {
     // two groups per step; one for the residual variant with two row tiles,
     // which keeps its registers within four waves per SIMD
@@ -191,8 +256,21 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
     __shared__ float red[kMaxDecodeWaves * MT * 256];
     __shared__ int tab[RES ? 8 * (kMaxGroups / 4) : 1];   // column block -> CSR position
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    if (QX) {
+        __shared__ float qred[kQaMaxWaves];
+        __shared__ uint8_t qfix[kQaMaxWaves][8 * kQaWords];
+        if (static_cast<int>(blockIdx.x) < a.M) {
+            quant_act_row(a.x, a.x_bf16, a.M, a.K, nullptr, a.xq_w, a.sx_w, blockIdx.x, tid, blockDim.x, qred, qfix);
+            // each wave's stores have reached its XCD's L2 before the barrier; the
+            // count's device-scope release then writes that L2 back
+            wait_all_memory();
+            __syncthreads();
+            if (tid == 0) __hip_atomic_fetch_add(&a.sync[kSyncCount], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+    }
     const int G = a.K / kGroup, G4 = (G + 3) / 4;
-    const int nt = blockIdx.x, n0 = nt * 16, n = n0 + (lane & 15);
+    const int nt = blockIdx.x - (QX ? a.M : 0), n0 = nt * 16, n = n0 + (lane & 15);
     const int br = n0 / a.bn, rrow = n - br * a.bn;
     const int q0 = wave * G4 / nw, q1 = (wave + 1) * G4 / nw;       // this wave's quads
     const int gb = 4 * q0, ge = min(4 * q1, G);                      // and groups
@@ -222,7 +300,7 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
     // two steps in flight: step i+1 is fetched while step i is multiplied
     // (ping-pong buffers, so no register copy waits on the prefetch)
     DecStep<MT, QS> s0, s1;
-    if (gb < ge) dec_fetch_main<MT, QS>(s0, src, gb, lane);
+    if (gb < ge) dec_fetch_main<MT, QS, !QX>(s0, src, gb, lane);
     if (RES) {
         // The zipper table of this wave's column blocks [2 gb, 2 ge), built by the
         // wave alone while its first loads are in flight: no workgroup barrier.
@@ -249,8 +327,48 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
         }
         if (gb < ge) dec_fetch_res<MT, QS, RES>(s0, a, src, tab, rrow, G, gb, lane);
     }
+    const int C = QX ? static_cast<int>(gridDim.x) - a.M : 0;   // column workgroups
+    if (QX) {
+        // the second step's weights, scales and residual rows go out before the wait too
+        if (gb + QS < ge) {
+            dec_fetch_main<MT, QS, false>(s1, src, gb + QS, lane);
+            if (RES) dec_fetch_res<MT, QS, RES>(s1, a, src, tab, rrow, G, gb + QS, lane);
+        }
+        if (tid == 0) {
+            int* const sy = a.sync;
+            int* const gave_up = &sy[kSyncGaveUp];
+            const int L = min(kSyncSlots, C);
+            // XCC id: hardware register 20, bits 3:0 (uniform over the workgroup)
+            const int xcc = static_cast<int>(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20)) & (kSyncSlots - 1);
+            int* const ready = &sync_slot(sy, xcc)[kSyncReady];
+            if (nt < L) {
+                spin_until(&sy[kSyncCount], a.M, gave_up);
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // this XCD's L2 holds no stale activations
+                __hip_atomic_store(ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                wait_all_memory();   // the flag is up before the check-in
+                __hip_atomic_fetch_add(&sy[kSyncLeaders], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                bool up = false;
+                for (int it = 0;; ++it) {
+                    if (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { up = true; break; }
+                    if (__hip_atomic_load(&sy[kSyncLeaders], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= L) break;
+                    if (it >= kSpinLimit) {
+                        __hip_atomic_store(gave_up, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(8);
+                }
+                // every leader has checked in, so every flag that will be raised is up
+                if (!up && !__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no leader ran on this XCD
+            }
+        }
+        __syncthreads();
+        if (gb < ge) dec_fetch_x<MT, QS>(s0, src, gb);
+        if (gb + QS < ge) dec_fetch_x<MT, QS>(s1, src, gb + QS);
+    }
     for (int g = gb; g < ge; g += 2 * QS) {
-        if (g + QS < ge) {
+        if (g + QS < ge && !(QX && g == gb)) {   // (the self-quantizing variant fetched step 1 early)
             dec_fetch_main<MT, QS>(s1, src, g + QS, lane);
             if (RES) dec_fetch_res<MT, QS, RES>(s1, a, src, tab, rrow, G, g + QS, lane);
         }
@@ -274,6 +392,37 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
         for (int w = 0; w < nw; ++w) v += red[((w * MT + t) * 4 + r) * 64 + l];
         const int m = t * 16 + (l >> 4) * 4 + r;
         if (m < a.M) store_out(a, OUTMODE, m, n0 + (l & 15), v);
+    }
+    if (QX && tid == 0) {
+        int* const sy = a.sync;
+        // A follower's accesses to the words were loads whose values it has used, so
+        // they are complete; a leader's check-in must land before its done count, so
+        // it waits (for its output stores too: 16 workgroups only).
+        if (nt < min(kSyncSlots, C)) wait_all_memory();
+        if (nt < C - 1) {
+            __hip_atomic_fetch_add(&sync_slot(sy, nt & (kSyncSlots - 1))[kSyncDone], 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            // the last column workgroup: every other one was dispatched before it and
+            // waits on nothing it holds, so their done counts all arrive
+            for (int it = 0;; ++it) {
+                int total = 0;
+                for (int i = 0; i < kSyncSlots; ++i)
+                    total += __hip_atomic_load(&sync_slot(sy, i)[kSyncDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (total >= C - 1) break;
+                if (it >= kSpinLimit) {
+                    __hip_atomic_store(&sy[kSyncGaveUp], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);   // the launch ends with this wait: poll closely
+            }
+            for (int i = 0; i < kSyncSlots; ++i) {
+                __hip_atomic_store(&sync_slot(sy, i)[kSyncReady], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&sync_slot(sy, i)[kSyncDone], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __hip_atomic_store(&sy[kSyncLeaders], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&sy[kSyncCount], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
@@ -724,6 +873,14 @@ static hipError_t go_wide(const GemmArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// one launch: M quantizing workgroups, then the column workgroups (M <= 32)
+template <int MT>
+static hipError_t go_decode_qx(const GemmArgs& a, hipStream_t st) {
+    const DecodePlan p = plan_decode(a.M, a.N, a.K);
+    k_gemm_decode<MT, true, false, 0, true><<<dim3(a.M + a.N / 16), dim3(64 * p.nw), 0, st>>>(a);
+    return hipGetLastError();
+}
+
 template <bool RES, bool DUMP, int OUT>
 static hipError_t go(const GemmArgs& a, hipStream_t st) {
     if (a.M <= 16) return go_decode<1, RES, DUMP, OUT>(a, st);
@@ -754,6 +911,8 @@ hipError_t launch_gemm(const GemmArgs& a, GemmKind kind, hipStream_t st) {
             return dump ? go<false, true, 0>(a, st) : go<false, false, 0>(a, st);
         case GemmKind::DenseToWorkspace:
             return go<false, false, 1>(a, st);
+        case GemmKind::FusedQuantAct:
+            return a.M <= 16 ? go_decode_qx<1>(a, st) : go_decode_qx<2>(a, st);
     }
     return hipErrorInvalidValue;
 }

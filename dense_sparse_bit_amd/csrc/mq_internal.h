@@ -21,9 +21,21 @@ struct GemmArgs {
     int y_bf16;
     int32_t* acc_dump;
     float* ws;
+    // the GEMM that quantizes its own activations: x [M][K] (fp32 or bf16), and
+    // where the codes and scales go (then read back as xq / sx), plus the
+    // producer/consumer counters (int32 [4], zero between calls)
+    const void* x;
+    int x_bf16;
+    uint8_t* xq_w;
+    float* sx_w;
+    int* sync;
 };
 
-enum class GemmKind { Fused, Dense, DenseToWorkspace };
+// int32 words of the self-quantizing GEMM's counter array: one 128-byte line for
+// the count of quantized tokens and the give-up flag, one per XCD slot (16)
+constexpr int kSyncWords = 32 * 17;
+
+enum class GemmKind { Fused, Dense, DenseToWorkspace, FusedQuantAct };
 
 // How the decode GEMM (M <= 32) is split: nw waves per workgroup share K.
 struct DecodePlan {

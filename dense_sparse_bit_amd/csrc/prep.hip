@@ -17,6 +17,7 @@
 
 #include "mq_device.h"
 #include "mq_internal.h"
+#include "mq_quant.h"
 
 namespace mq {
 
@@ -66,131 +67,16 @@ __global__ __launch_bounds__(256) void k_hessian(const void* __restrict__ x, int
 }
 
 // ---------------------------------------------------------------------------
-// a4: per-token symmetric int4 quantization. One workgroup per token; each
-// thread owns code words (8 consecutive inputs each) and keeps their values in
-// registers between the exact max-reduction of |x| (order-free) and the
-// quantization, so x is read once. Words are stored group-major
-// ([K/128][M][64 B]), the layout the GEMM loads from.
+// a4: per-token symmetric int4 quantization, one workgroup per token (the body
+// is quant_act_row in mq_quant.h, shared with the GEMM that quantizes its own
+// activations).
 // ---------------------------------------------------------------------------
-constexpr int kQaWords = 4;     // words kept in registers per thread (K <= 8192 read once)
-
-__device__ __forceinline__ void load8(const void* row, bool bf16, int64_t j, float (&v)[8],
-                                      const float* __restrict__ colscale) {
-    if (bf16) {
-        const uint4 u = static_cast<const uint4*>(row)[j];
-        const uint32_t p[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(p[i] << 16);
-            v[2 * i + 1] = __uint_as_float(p[i] & 0xffff0000u);
-        }
-    } else {
-        const float4 a = static_cast<const float4*>(row)[2 * j];
-        const float4 b = static_cast<const float4*>(row)[2 * j + 1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    }
-    // migrated activations: x^ = fp32(x * r_k), one rounding per element
-    if (colscale) {
-        const float4 a = reinterpret_cast<const float4*>(colscale)[2 * j];
-        const float4 b = reinterpret_cast<const float4*>(colscale)[2 * j + 1];
-        v[0] = v[0] * a.x; v[1] = v[1] * a.y; v[2] = v[2] * a.z; v[3] = v[3] * a.w;
-        v[4] = v[4] * b.x; v[5] = v[5] * b.y; v[6] = v[6] * b.z; v[7] = v[7] * b.w;
-    }
-}
-
 __global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, int bf16, int64_t M, int64_t K,
                                                    const float* __restrict__ colscale,
                                                    uint8_t* __restrict__ xq, float* __restrict__ sx) {
-    const int64_t m = blockIdx.x, W = K / 8;
-    const void* row = bf16 ? static_cast<const void*>(static_cast<const uint16_t*>(x) + m * K)
-                           : static_cast<const void*>(static_cast<const float*>(x) + m * K);
-    const int t = threadIdx.x;
-    __shared__ float red[4];
-    __shared__ uint8_t fixb[4][8 * kQaWords];   // per-wave codes of a repaired lane
-    float v[kQaWords][8];
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kQaWords; ++i) {
-        const int64_t j = t + 256 * i;
-        if (j < W) {
-            load8(row, bf16, j, v[i], colscale);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[i][e]));
-    }
-    for (int64_t j = t + 256 * kQaWords; j < W; j += 256) {
-        float u[8];
-        load8(row, bf16, j, u, colscale);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(u[e]));
-    }
-    for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
-    if ((t & 63) == 0) red[t >> 6] = a;
-    __syncthreads();
-    a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float s = a / 7.0f;
-    const float rs = s == 0.0f ? 0.0f : 1.0f / s;
-    if (t == 0) sx[m] = s;
-    // group-major output: word j (inputs 8j..8j+7) is bytes 4(j%16).. of group j/16's chunk
-    auto dst = [&](int64_t j) { return reinterpret_cast<uint32_t*>(xq + xq_row(j >> 4, M, m) + (j & 15) * 4); };
-    // branch-free codes for the values held in registers; rare near-ties (or a
-    // non-finite reciprocal) redo them with the exact quantizer
-    uint32_t nib[kQaWords];
-    float worst = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kQaWords; ++i) {
-        nib[i] = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            nib[i] |= (static_cast<uint32_t>(static_cast<int>(rtn_fast(v[i][e], rs, worst))) & 15u) << (4 * e);
-    }
-    const bool redo = !(worst < kFastMargin) || !(fabsf(rs) <= 3.0e38f);
-    // Rare: a quotient within 4e-6 of a rounding boundary. The wave repairs each
-    // flagged lane L together: lane i < 32 recodes L's value i exactly, and L
-    // gathers the codes through LDS.
-    uint64_t flagged = __ballot(redo);
-    while (flagged) {
-        const int L = __builtin_ctzll(flagged);
-        flagged &= flagged - 1;
-        const int tL = (t & ~63) + L, l = t & 63;
-        if (l < 8 * kQaWords) {
-            const int64_t j = tL + 256 * (l >> 3);
-            uint8_t c = 0;
-            if (j < W) {
-                float u[8];
-                load8(row, bf16, j, u, colscale);
-                c = static_cast<uint8_t>(static_cast<int>(rtn_codef(u[l & 7], s, rs)) & 15);
-            }
-            fixb[t >> 6][l] = c;
-        }
-        __builtin_amdgcn_wave_barrier();
-        if (l == L) {
-#pragma unroll
-            for (int i = 0; i < kQaWords; ++i) {
-                nib[i] = 0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) nib[i] |= static_cast<uint32_t>(fixb[t >> 6][8 * i + e]) << (4 * e);
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-    }
-#pragma unroll
-    for (int i = 0; i < kQaWords; ++i) {
-        const int64_t j = t + 256 * i;
-        if (j < W) *dst(j) = code_word(nib[i]);
-    }
-    for (int64_t j = t + 256 * kQaWords; j < W; j += 256) {
-        float u[8];
-        load8(row, bf16, j, u, colscale);
-        uint32_t n8 = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) n8 |= (static_cast<uint32_t>(static_cast<int>(rtn_codef(u[e], s, rs))) & 15u) << (4 * e);
-        *dst(j) = code_word(n8);
-    }
+    __shared__ float red[kQaMaxWaves];
+    __shared__ uint8_t fixb[kQaMaxWaves][8 * kQaWords];
+    quant_act_row(x, bf16, M, K, colscale, xq, sx, blockIdx.x, threadIdx.x, blockDim.x, red, fixb);
 }
 
 // ---------------------------------------------------------------------------

@@ -235,6 +235,40 @@ int mq_gemm_w4a4_residual_mapped(const uint8_t* xq, const float* sx, const uint8
                                  int bk, void* y, int y_dtype, int32_t* acc_dump, void* stream);
 
 /*
+ * The fused GEMM that also quantizes its activations (Methodology 3 schedules
+ * quantization as a stage of the same pipeline as the dense and sparse products):
+ * y = mq_gemm_w4a4_residual_mapped applied to mq_quantize_act(x), with xq and sx
+ * written as mq_quantize_act writes them (same bits), and y bit-identical to the
+ * two calls in sequence.
+ * It runs either as one launch (M <= 32): its first M workgroups quantize one
+ * token each while the output-column workgroups wait for them (counters in
+ * `sync`) before reading any activation; or as two launches on `stream`,
+ * mq_quantize_act and then the GEMM. `launch` picks: MQ_ACT_ONE_LAUNCH (M > 32
+ * is then an invalid argument), MQ_ACT_TWO_LAUNCHES, or MQ_ACT_AUTO, which takes
+ * one launch when M <= 32 and M N <= 8 K (where it measured faster on MI355X: a
+ * few long rows over few columns) and two otherwise. Both give the same bits.
+ * x: [M][K] fp32 or bf16 (x_dtype), 16-byte aligned; xq, sx: outputs as in
+ * mq_quantize_act; rmap, rq, nnz: as in mq_gemm_w4a4_residual_mapped (rmap required).
+ * sync (required when the one-launch form runs, else unused and may be null):
+ * int32 [MQ_SYNC_WORDS] device array, all zero before the first call (e.g.
+ * zero-filled once); every completed call leaves it zero again, so it needs no
+ * clearing between calls and the call can be captured in a HIP graph. It holds the
+ * count of quantized tokens, a check-in count and, in one 128-byte line per XCD
+ * slot, a ready flag and a count of finished column workgroups. sync[2] becomes 1
+ * if a workgroup ever gave up waiting (after well under a few seconds; never
+ * expected) and stays 1 until the caller clears it. Calls that share one sync
+ * array must not overlap (order them on one stream).
+ */
+#define MQ_SYNC_WORDS 544
+#define MQ_ACT_AUTO 0
+#define MQ_ACT_ONE_LAUNCH 1
+#define MQ_ACT_TWO_LAUNCHES 2
+int mq_gemm_w4a4_residual_act(const void* x, int x_dtype, const uint8_t* wq, const uint16_t* sw,
+                              const int32_t* rmap, const uint8_t* rq, int64_t nnz, int64_t M,
+                              int64_t N, int64_t K, int group, int bn, int bk, uint8_t* xq,
+                              float* sx, int32_t* sync, int launch, void* y, int y_dtype, void* stream);
+
+/*
  * Dense-only 4-bit GEMM: the same kernel with the residual path compiled out
  * (the "dense 4-bit GEMM kernel" the residual is fused into, Methodology 3).
  * y = sx * sum_g s * P. With nnz == 0 the fused call gives the same bits.

@@ -35,6 +35,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for fn in ["mq_quantize_act", "mq_pack_weights", "mq_select_blocks", "mq_gemm_w4a4_residual",
                "mq_select_workspace_bytes", "mq_block_map", "mq_gemm_w4a4_residual_mapped",
+               "mq_gemm_w4a4_residual_act",
                "mq_hessian_diag", "mq_gemm_w4a4_dense", "mq_gemm_residual_separate",
                "mq_status_string", "mq_version"]:
         assert fn in names
@@ -141,6 +142,39 @@ def test_preparation_calls_reject_bad_arguments(lib_nogpu):
     assert mapped(nnz=nb + 1) == -1
     assert mapped(K=320) == -2
     assert mapped(N=1 << 17, K=65536, bn=128, nnz=(1 << 31) // (128 * 32) + 1) == -2
+    # the self-quantizing GEMM: activations, map and (for M <= 32) the counters are required
+    act = lambda **kw: lib.mq_gemm_w4a4_residual_act(
+        kw.get("x", FAKE), kw.get("xd", 1), FAKE, FAKE, kw.get("rmap", FAKE), FAKE, 3, kw.get("M", 4),
+        512, kw.get("K", 512), 128, 64, 64, FAKE, FAKE, kw.get("sync", FAKE), kw.get("launch", 1), FAKE, 1,
+        None)
+    assert act(x=None) == -1
+    assert act(x=FAKE + 8) == -1
+    assert act(xd=5) == -1
+    assert act(rmap=None) == -1
+    assert act(sync=None) == -1
+    assert act(sync=FAKE + 2) == -1
+    assert act(launch=3) == -1 and act(launch=-1) == -1
+    assert act(M=33) == -1, "one launch takes at most 32 tokens"
+    # "auto" takes one launch only for M <= 32 and M N <= 8 K: then the counters are required
+    assert act(launch=0, M=4, K=512, sync=None) == -1
+    assert act(M=0, x=None, sync=None) == 0
+
+
+def test_act_launch_rule(mq):
+    """The binding's copy of the library's "auto" rule for the self-quantizing GEMM
+    (one launch iff M <= 32 and M N <= 8 K), on the decode shapes it was measured on,
+    and the header's constants as the binding uses them."""
+    txt = open(HEADER).read()
+    defs = dict(re.findall(r"#define (MQ_[A-Z_]+) (\d+)", txt))
+    assert int(defs["MQ_SYNC_WORDS"]) == mq.SYNC_WORDS
+    assert [int(defs[k]) for k in ("MQ_ACT_AUTO", "MQ_ACT_ONE_LAUNCH", "MQ_ACT_TWO_LAUNCHES")] == \
+        [mq._ACT_LAUNCH[k] for k in ("auto", "one", "two")]
+    rule = mq.act_one_launch
+    assert rule(4, 4096, 14336) and rule(32, 5120, 25600)                # down projections
+    assert not rule(32, 4096, 14336) and not rule(16, 4096, 4096)        # M N / K = 9.1, 16
+    assert not rule(4, 14336, 4096) and not rule(32, 25600, 5120)        # up projections
+    assert not rule(33, 1, 1 << 20), "one launch takes at most 32 tokens"
+    assert rule(64, 1, 1, "one") and not rule(1, 1, 1 << 20, "two")
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -173,6 +173,19 @@ def _check(mq, orc, inp, k_blocks, out_dtype_name="bf16", rows=None, check_varia
     assert torch.equal(bits(ymd), bits(yp))
     md = mdump[sel] if rows is None else mdump[torch.as_tensor(rows, device="cuda")]
     np.testing.assert_array_equal(_np(md).astype(np.int64), ref["T"])
+    # the GEMM that quantizes its own activations, in both forms (one launch up to 32
+    # tokens, and two launches): the same codes and scales as the quantization call,
+    # the mapped call's y bits, and the counters back at zero; twice each, so the
+    # second one-launch call runs on the reset counters
+    sync = mq.sync_words()
+    for launch in (("one", "two", "auto") if cfg.M <= 32 else ("two", "auto")):
+        for _ in range(2):
+            ya, xqa, sxa = mq.gemm_w4a4_residual_act(g["x"], g["wq"], g["sw"], rmap, g["rq"], cfg.K, bn=cfg.bn,
+                                                     out_dtype=out_dtype, sync=sync, launch=launch)
+            torch.cuda.synchronize()
+            assert torch.equal(xqa, g["xq"]) and torch.equal(sxa, g["sx"]), f"quantization differs ({launch})"
+            assert torch.equal(bits(ya), bits(ym)), f"the self-quantizing call ({launch}) differs from quantize + GEMM"
+            assert not sync.any(), f"counters not reset: {sync.tolist()}"
     if check_variants:
         # dense-only kernel: T = 14 P, and y equals the fused kernel with no residual
         ddump = torch.empty_like(g["dump"])
