@@ -246,19 +246,20 @@ def leg_record(cfg, pct, k_blocks, t):
     return rec
 
 
-def read_ceiling_us(torch, nbytes, calls=100):
-    """Time of a plain streaming read of `nbytes` (torch's sum over a float32 view),
-    over rotating slices of a 1 GiB buffer: the achievable read rate at this size."""
-    n = max(64, int(nbytes) // 4)
-    src = torch.ones((1 << 30) // 4, dtype=torch.float32, device="cuda")
-    slices = max(1, src.numel() // n)
-    out = torch.empty((), dtype=torch.float32, device="cuda")
+def read_ceiling_us(mq, torch, nbytes, calls=100):
+    """Time of a plain streaming read of `nbytes` (the library's read probe: 16-byte
+    loads, four in flight per lane) over rotating slices of a 1 GiB buffer, as a
+    graph of back-to-back launches: the read rate a kernel reaches at this size."""
+    n = max(16, (int(nbytes) + 15) // 16 * 16)
+    src = torch.ones((1 << 30) // 4, dtype=torch.int32, device="cuda")
+    slices = max(1, (1 << 30) // n)
+    out = torch.empty(mq.READ_PROBE_WORDS, dtype=torch.int32, device="cuda")
+    views = [src.view(torch.uint8)[j * n:(j + 1) * n] for j in range(slices)]
 
     def rd(i):
-        j = i % slices
-        torch.sum(src[j * n:(j + 1) * n], dim=0, out=out)
+        mq.read_probe(views[i % slices], n, out=out)
     us = _graph_time_us(torch, rd, calls)
-    del src
+    del src, views
     torch.cuda.empty_cache()
     return us
 
@@ -643,7 +644,7 @@ def main():
             if c.name == cfg.name:
                 continue
             lay = Layer(mq, torch, c)
-            rc = read_ceiling_us(torch, gemm_bytes(c, c.k_blocks(10)))
+            rc = read_ceiling_us(mq, torch, gemm_bytes(c, c.k_blocks(10)))
             for b in budgets:
                 tb = bench_variants(mq, torch, lay, c.k_blocks(b), args.gemm_calls, bf16=(b == 10))
                 tb["read_ceiling_us"] = rc

@@ -44,6 +44,7 @@ _SIGS = {
                               _p, _int, _p, _p],
     "mq_gemm_w4a4_dense": [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p, _int, _p, _p],
     "mq_block_map": [_p, _p, _i64, _i64, _i64, _int, _int, _p, _p],
+    "mq_read_probe": [_p, _i64, _p, _p],
     "mq_gemm_w4a4_residual_act": [_p, _int, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
                                   _p, _p, _p, _int, _p, _int, _p],
     "mq_gemm_w4a4_residual_mapped": [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
@@ -471,6 +472,25 @@ def gemm_w4a4_residual_act(x, wq, sw, rmap, rq, K: int, bn: int = 64, out_dtype=
           _ptr(rq) if nnz else None, nnz, M, N, K, GROUP, bn, BK, _ptr(xq), _ptr(sx),
           _ptr(sync) if one else None, _ACT_LAUNCH[launch], _ptr(y), _y_dtype(y.dtype), _stream(stream))
     return y, xq, sx
+
+
+READ_PROBE_WORDS = 8192   # MQ_READ_PROBE_WORDS
+
+
+def read_probe(buf, nbytes: int = None, out=None, stream=None):
+    """Streaming read of the first nbytes of buf (a measurement aid: the read rate a
+    kernel reaches at that byte count). Returns the uint32 output words."""
+    _device_contig(buf, "buf")
+    have = buf.numel() * buf.element_size()
+    nbytes = have if nbytes is None else int(nbytes)
+    if nbytes < 0 or nbytes > have or nbytes % 16:
+        raise ValueError(f"nbytes must be a multiple of 16 within the buffer's {have} bytes, got {nbytes}")
+    if out is None:
+        out = torch.empty(READ_PROBE_WORDS, dtype=torch.int32, device=buf.device)
+    _buf(out, "out", 4 * READ_PROBE_WORDS, _I32)
+    _on_device(buf=buf, out=out)
+    _call("mq_read_probe", _ptr(buf), nbytes, _ptr(out), _stream(stream))
+    return out
 
 
 def gemm_w4a4_dense(xq, sx, wq, sw, K: int, out_dtype=torch.bfloat16, y=None, acc_dump=None,

@@ -306,6 +306,14 @@ int mq_gemm_w4a4_residual_act(const void* x, int x_dtype, const uint8_t* wq, con
     return hip_status(mq::launch_gemm(a, mq::GemmKind::FusedQuantAct, st));
 }
 
+static_assert(mq::kReadProbeMaxBlocks == MQ_READ_PROBE_WORDS, "read probe output size");
+
+int mq_read_probe(const void* p, int64_t bytes, uint32_t* out, void* stream) {
+    if (bytes < 0 || (bytes & 15) || (bytes > 0 && (!p || !aligned16(p))) || !out) return MQ_ERR_INVALID_ARG;
+    if (bytes == 0) return MQ_OK;
+    return hip_status(mq::launch_read_probe(p, bytes, out, static_cast<hipStream_t>(stream)));
+}
+
 int mq_gemm_w4a4_dense(const uint8_t* xq, const float* sx, const uint8_t* wq, const uint16_t* sw,
                        int64_t M, int64_t N, int64_t K, int group, void* y, int y_dtype,
                        int32_t* acc_dump, void* stream) {

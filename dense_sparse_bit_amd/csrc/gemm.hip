@@ -53,7 +53,8 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int OUTMODE, int m,
 // HBM, limits this shape class: every load instruction counts, hence 1 KB per
 // instruction for weights and activations and one scale load per quad.
 // ===========================================================================
-constexpr int kMaxDecodeWaves = 8;
+constexpr int kMaxDecodeWaves = 16;
+static_assert(kMaxDecodeWaves <= kQaMaxWaves, "the quantizing workgroups run with the decode block size");
 constexpr int kMaxGroups = 512;    // K <= 65536
 
 // One pipeline step: QS consecutive groups (QS = 4 for one row tile of tokens,
@@ -253,7 +254,9 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
     // two groups per step; one for the residual variant with two row tiles,
     // which keeps its registers within four waves per SIMD
     constexpr int QS = (RES && MT == 2) ? 1 : 2;
-    __shared__ float red[kMaxDecodeWaves * MT * 256];
+    // per-wave partial sums for the final reduction: nw * MT * 256 floats, sized at
+    // launch so that a plan with few waves does not pay LDS (occupancy) for many
+    extern __shared__ float red[];
     __shared__ int tab[RES ? 8 * (kMaxGroups / 4) : 1];   // column block -> CSR position
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
     if (QX) {
@@ -857,10 +860,15 @@ __global__ __launch_bounds__(256) void k_residual_merge(GemmArgs a) {
 // ===========================================================================
 // launch selection
 // ===========================================================================
+template <int MT>
+static size_t decode_red_bytes(const DecodePlan& p) {
+    return static_cast<size_t>(p.nw) * MT * 256 * sizeof(float);
+}
+
 template <int MT, bool RES, bool DUMP, int OUT>
 static hipError_t go_decode(const GemmArgs& a, hipStream_t st) {
     const DecodePlan p = plan_decode(a.M, a.N, a.K);
-    k_gemm_decode<MT, RES, DUMP, OUT><<<dim3(a.N / 16), dim3(64 * p.nw), 0, st>>>(a);
+    k_gemm_decode<MT, RES, DUMP, OUT><<<dim3(a.N / 16), dim3(64 * p.nw), decode_red_bytes<MT>(p), st>>>(a);
     return hipGetLastError();
 }
 
@@ -877,7 +885,7 @@ static hipError_t go_wide(const GemmArgs& a, hipStream_t st) {
 template <int MT>
 static hipError_t go_decode_qx(const GemmArgs& a, hipStream_t st) {
     const DecodePlan p = plan_decode(a.M, a.N, a.K);
-    k_gemm_decode<MT, true, false, 0, true><<<dim3(a.M + a.N / 16), dim3(64 * p.nw), 0, st>>>(a);
+    k_gemm_decode<MT, true, false, 0, true><<<dim3(a.M + a.N / 16), dim3(64 * p.nw), decode_red_bytes<MT>(p), st>>>(a);
     return hipGetLastError();
 }
 
@@ -889,15 +897,20 @@ static hipError_t go(const GemmArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode plan: waves per workgroup. The grid has one workgroup per 16 columns;
-// about 2048 waves in total keep enough loads in flight on all 256 CUs, with at
-// least one quad per wave. The plan depends on (M, N, K) only, so the fused and
-// the dense-only kernels of a shape sum in the same order.
+// Decode plan: waves per workgroup. The grid has one workgroup per 16 columns,
+// and each wave keeps two steps of loads in flight, so the time is about the
+// steps per wave over two, times the load latency, as long as every workgroup is
+// resident at once. With at most 256 column workgroups (one per CU or fewer) a
+// workgroup takes 16 waves, so each wave's share of K is short (measured on the
+// 4096-column shapes: 11-15% faster than 8 waves). With more, about 2048 waves in
+// total: more waves there gave slower launches (measured at 14336 and 25600
+// columns). Each wave gets at least one quad. The plan depends on (M, N, K) only,
+// so the fused and the dense-only kernels of a shape sum in the same order.
 // ---------------------------------------------------------------------------
 DecodePlan plan_decode(int M, int N, int K) {
     (void)M;
     const int G4 = (K / kGroup + 3) / 4, subtiles = N / 16;
-    int nw = subtiles > 0 ? (2048 + subtiles - 1) / subtiles : 1;
+    int nw = subtiles <= 256 ? kMaxDecodeWaves : (2048 + subtiles - 1) / subtiles;
     nw = std::max(1, std::min(nw, std::min(kMaxDecodeWaves, G4)));
     return DecodePlan{nw};
 }

@@ -68,6 +68,10 @@ hipError_t launch_pack(const float* w, int64_t N, int64_t K, int bn, const int32
 hipError_t launch_block_map(const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz, int64_t N, int64_t K,
                             int bn, int32_t* rmap, hipStream_t st);
 hipError_t launch_gemm(const GemmArgs& a, GemmKind kind, hipStream_t st);
+// streaming-read probe: at most kReadProbeMaxBlocks workgroups, one output word each
+constexpr int kReadProbeMaxBlocks = 8192;
+int read_probe_blocks(int64_t bytes);
+hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* out, hipStream_t st);
 hipError_t launch_residual_merge(const GemmArgs& a, hipStream_t st);
 
 }  // namespace mq

@@ -12,7 +12,7 @@
 namespace mq {
 
 constexpr int kQaWords = 4;      // words kept in registers per thread
-constexpr int kQaMaxWaves = 8;   // workgroups of up to 512 threads
+constexpr int kQaMaxWaves = 16;  // workgroups of up to 1024 threads
 
 __device__ __forceinline__ void load8(const void* row, bool bf16, int64_t j, float (&v)[8],
                                       const float* __restrict__ colscale) {

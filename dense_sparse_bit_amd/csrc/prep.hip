@@ -591,4 +591,39 @@ hipError_t launch_pack(const float* w, int64_t N, int64_t K, int bn, const int32
     return hipGetLastError();
 }
 
+// A plain streaming read of n16 16-byte words: the HBM read rate a kernel reaches
+// at a given byte count (what the decode GEMM, which streams its weights once, is
+// held against). Each lane keeps four loads in flight; each workgroup writes one
+// word (the XOR of what it read) so the loads stay live.
+__global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p, int64_t n16,
+                                                    uint32_t* __restrict__ out) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 a = p[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off);
+    __shared__ uint32_t w[4];
+    if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = w[0] ^ w[1] ^ w[2] ^ w[3];
+}
+
+int read_probe_blocks(int64_t bytes) {
+    const int64_t n16 = bytes / 16;
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((n16 + 1023) / 1024, kReadProbeMaxBlocks)));
+}
+
+hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* out, hipStream_t st) {
+    k_read_probe<<<dim3(static_cast<unsigned>(read_probe_blocks(bytes))), dim3(256), 0, st>>>(
+        static_cast<const uint4*>(p), bytes / 16, out);
+    return hipGetLastError();
+}
+
 }  // namespace mq

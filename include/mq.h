@@ -269,6 +269,18 @@ int mq_gemm_w4a4_residual_act(const void* x, int x_dtype, const uint8_t* wq, con
                               float* sx, int32_t* sync, int launch, void* y, int y_dtype, void* stream);
 
 /*
+ * Measurement aid, not a step of the method: a plain streaming read of `bytes`
+ * bytes at p (16-byte aligned, bytes a multiple of 16), the HBM read rate a kernel
+ * reaches at that byte count. The decode GEMM streams its weights once, so this
+ * is the ceiling its time is compared with (the Experimental Results measure
+ * decode overheads against the dense kernel; this measures both against memory).
+ * out: uint32 [MQ_READ_PROBE_WORDS] device array; each workgroup writes the XOR of
+ * the words it read to one entry (the values mean nothing). Asynchronous.
+ */
+#define MQ_READ_PROBE_WORDS 8192
+int mq_read_probe(const void* p, int64_t bytes, uint32_t* out, void* stream);
+
+/*
  * Dense-only 4-bit GEMM: the same kernel with the residual path compiled out
  * (the "dense 4-bit GEMM kernel" the residual is fused into, Methodology 3).
  * y = sx * sum_g s * P. With nnz == 0 the fused call gives the same bits.

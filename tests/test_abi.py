@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for fn in ["mq_quantize_act", "mq_pack_weights", "mq_select_blocks", "mq_gemm_w4a4_residual",
                "mq_select_workspace_bytes", "mq_block_map", "mq_gemm_w4a4_residual_mapped",
-               "mq_gemm_w4a4_residual_act",
+               "mq_gemm_w4a4_residual_act", "mq_read_probe",
                "mq_hessian_diag", "mq_gemm_w4a4_dense", "mq_gemm_residual_separate",
                "mq_status_string", "mq_version"]:
         assert fn in names
@@ -158,6 +158,15 @@ def test_preparation_calls_reject_bad_arguments(lib_nogpu):
     # "auto" takes one launch only for M <= 32 and M N <= 8 K: then the counters are required
     assert act(launch=0, M=4, K=512, sync=None) == -1
     assert act(M=0, x=None, sync=None) == 0
+
+
+def test_read_probe_rejections(lib_nogpu):
+    probe = lambda p=FAKE, n=4096, out=FAKE: lib_nogpu.mq_read_probe(p, n, out, None)
+    assert probe(n=4004) == -1                  # not a multiple of 16
+    assert probe(p=FAKE + 8) == -1               # unaligned
+    assert probe(p=None) == -1 and probe(out=None) == -1
+    assert probe(n=-16) == -1
+    assert probe(n=0, p=None) == 0
 
 
 def test_act_launch_rule(mq):
