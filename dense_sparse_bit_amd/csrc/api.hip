@@ -282,9 +282,9 @@ int mq_gemm_w4a4_residual_act(const void* x, int x_dtype, const uint8_t* wq, con
     if (launch == MQ_ACT_ONE_LAUNCH && M > 32) return MQ_ERR_INVALID_ARG;
     // measured crossover on MI355X: the one-launch form's wait grows with the
     // tokens and the column workgroups (M N), the stand-alone quantization with the
-    // row length (K); one launch measured faster up to M N / K = 6.4 and slower
-    // from 9.1 on, so the rule splits at 8
-    const bool one = launch == MQ_ACT_ONE_LAUNCH || (launch == MQ_ACT_AUTO && M <= 32 && M * N <= 8 * K);
+    // row length (K); one launch measured faster up to M N / K = 9.1 and slower
+    // from 14 on, so the rule splits at 12
+    const bool one = launch == MQ_ACT_ONE_LAUNCH || (launch == MQ_ACT_AUTO && M <= 32 && M * N <= 12 * K);
     if (M == 0) return MQ_OK;
     if (!x || !aligned16(x) || (one && (!sync || (reinterpret_cast<uintptr_t>(sync) & 3u))))
         return MQ_ERR_INVALID_ARG;

@@ -155,7 +155,7 @@ def test_preparation_calls_reject_bad_arguments(lib_nogpu):
     assert act(sync=FAKE + 2) == -1
     assert act(launch=3) == -1 and act(launch=-1) == -1
     assert act(M=33) == -1, "one launch takes at most 32 tokens"
-    # "auto" takes one launch only for M <= 32 and M N <= 8 K: then the counters are required
+    # "auto" takes one launch only for M <= 32 and M N <= 12 K: then the counters are required
     assert act(launch=0, M=4, K=512, sync=None) == -1
     assert act(M=0, x=None, sync=None) == 0
 
@@ -171,7 +171,7 @@ def test_read_probe_rejections(lib_nogpu):
 
 def test_act_launch_rule(mq):
     """The binding's copy of the library's "auto" rule for the self-quantizing GEMM
-    (one launch iff M <= 32 and M N <= 8 K), on the decode shapes it was measured on,
+    (one launch iff M <= 32 and M N <= 12 K), on the decode shapes it was measured on,
     and the header's constants as the binding uses them."""
     txt = open(HEADER).read()
     defs = dict(re.findall(r"#define (MQ_[A-Z_]+) (\d+)", txt))
@@ -180,7 +180,8 @@ def test_act_launch_rule(mq):
         [mq._ACT_LAUNCH[k] for k in ("auto", "one", "two")]
     rule = mq.act_one_launch
     assert rule(4, 4096, 14336) and rule(32, 5120, 25600)                # down projections
-    assert not rule(32, 4096, 14336) and not rule(16, 4096, 4096)        # M N / K = 9.1, 16
+    assert rule(32, 4096, 14336)                                         # M N / K = 9.1
+    assert not rule(16, 4096, 4096) and not rule(4, 14336, 4096)         # 16, 14
     assert not rule(4, 14336, 4096) and not rule(32, 25600, 5120)        # up projections
     assert not rule(33, 1, 1 << 20), "one launch takes at most 32 tokens"
     assert rule(64, 1, 1, "one") and not rule(1, 1, 1 << 20, "two")
