@@ -425,6 +425,25 @@ def pmc_pass(mq, torch, cfg, k_blocks, calls=5):
     torch.cuda.synchronize()
 
 
+def trace_pass(mq, torch, cfg, k_blocks, calls=100):
+    """What a per-shape `rocprofv3 --kernel-trace` runs: `calls` fused GEMM calls (block
+    map), then `calls` dense-only calls of the workload, eagerly, over rotated weight
+    copies (as the GEMM legs), so each kernel's average is that of cold weights."""
+    layer = Layer(mq, torch, cfg)
+    p = layer.pack(k_blocks)
+    sets = layer.copies(p, gemm_bytes(cfg, k_blocks))
+    n = len(sets)
+    y = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device="cuda")
+    for i in range(calls):
+        s = sets[i % n]
+        mq.gemm_w4a4_residual(layer.xq, layer.sx, s["wq"], s["sw"], s["row_ptr"], s["col_idx"], s["rq"],
+                              cfg.K, bn=cfg.bn, y=y, rmap=s["rmap"])
+    for i in range(calls):
+        s = sets[i % n]
+        mq.gemm_w4a4_dense(layer.xq, layer.sx, s["wq"], s["sw"], cfg.K, y=y)
+    torch.cuda.synchronize()
+
+
 def _db(path):
     import glob
     import sqlite3
@@ -591,6 +610,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="batch sweep + layer stack, one JSON line")
+    ap.add_argument("--trace-pass", action="store_true",
+                    help="eager fused then dense calls of --workload over rotated copies (for a kernel trace)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="a few GEMM calls and a copy of known size (for rocprofv3 --pmc), print nothing")
     ap.add_argument("--profile-summary", metavar="DB", help="print a rocprofv3 kernel-trace summary")
@@ -623,6 +644,9 @@ def main():
     cfg = synth.CONFIGS[args.workload]
     pct = cfg.default_budget if args.budget is None else args.budget
     k_blocks = cfg.k_blocks(pct)
+    if args.trace_pass:
+        trace_pass(mq, torch, cfg, k_blocks)
+        return
     if args.pmc_pass:
         pmc_pass(mq, torch, cfg, k_blocks)
         return
