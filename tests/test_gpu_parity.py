@@ -282,6 +282,48 @@ def test_degenerate_rows_and_groups(mq, orc):
     _check(mq, orc, inp, 7, "bf16")
 
 
+@pytest.mark.parametrize("launch", ["one", "two"])
+def test_self_quantizing_gemm_in_a_graph(mq, launch):
+    """The self-quantizing GEMM captured in a HIP graph and replayed several times,
+    with eager work and synchronizations between replays: every replay gives the
+    eager call's y, codes and scales bit for bit, and (one launch) leaves its
+    counters zero, so replays need no clearing."""
+    import torch
+    cfg = synth.custom_config("graph_act", M=4, K=2048, N=512, bn=64)
+    say(f"[graph] self-quantizing GEMM, launch={launch}, M={cfg.M} K={cfg.K} N={cfg.N}")
+    inp = _inputs(cfg)
+    x = torch.from_numpy(inp.X).cuda()
+    w = torch.from_numpy(inp.W).cuda()
+    g = mq.forward_layer(x, w, cfg.k_blocks(10), bn=cfg.bn)
+    rmap = mq.block_map(g["row_ptr"], g["col_idx"], cfg.N, cfg.K, bn=cfg.bn)
+    sync = mq.sync_words()
+    call = lambda **kw: mq.gemm_w4a4_residual_act(x, g["wq"], g["sw"], rmap, g["rq"], cfg.K, bn=cfg.bn,
+                                                  sync=sync, launch=launch, **kw)
+    ye, xqe, sxe = call()
+    torch.cuda.synchronize()
+    assert torch.equal(xqe, g["xq"]) and torch.equal(sxe, g["sx"])
+    y, xq, sx = torch.empty_like(ye), torch.empty_like(xqe), torch.empty_like(sxe)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(y=y, xq=xq, sx=sx)           # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        call(y=y, xq=xq, sx=sx)
+    noise = torch.randn(1 << 20, device="cuda")
+    for r in range(4):
+        y.zero_(); xq.zero_(); sx.zero_()
+        noise.mul_(1.0001)                # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ye.view(torch.int16)), f"replay {r}: y differs"
+        assert torch.equal(xq, xqe) and torch.equal(sx, sxe), f"replay {r}: codes or scales differ"
+        assert not sync.any(), f"replay {r}: counters not reset: {sync.nonzero().flatten().tolist()}"
+
+
 def test_zero_tokens_no_op(mq):
     import torch
     xq = torch.empty((4, 0, 64), dtype=torch.uint8, device="cuda")
