@@ -760,6 +760,12 @@ __global__ __launch_bounds__(64 * NWN, DUMP ? 1 : 2) void k_gemm_wide(GemmArgs a
     auto step = [&](int g, const uint4 (&Bc)[2][2], uint4 (&Bn)[2][2], const uint32_t (&Sc)[2],
                     uint32_t (&Sn)[2]) __attribute__((always_inline)) {
         const int st = g % kStages;
+        // Each SIMD runs two of these waves. While one issues its MFMAs (the previous
+        // group's residual and this group's base products) it takes issue priority
+        // over the other, which is then in its loads, widening or barrier: the MFMA
+        // pipe idles less (measured: fused 219 -> 214 us, dense 190 -> 179 us on the
+        // Qwen3-14B prefill shape).
+        __builtin_amdgcn_s_setprio(1);
         if (RES && R.rmask) {
             __asm__ volatile("" ::: "memory");
             residual(g - 1, (g + kStages - 1) % kStages, R, Sn);   // Sn still holds group g - 1's scales
@@ -769,6 +775,7 @@ __global__ __launch_bounds__(64 * NWN, DUMP ? 1 : 2) void k_gemm_wide(GemmArgs a
         for (int j = 0; j < 2; ++j) Sn[j] = load_scale(g + 2, j);
         if (RES) load_res(g, R);
         compute(g, st, Bc, Sc);
+        __builtin_amdgcn_s_setprio(0);
         store_x(X, (g + 1) % kStages);
         load_x(g + 2, X);
         schedule_step();
