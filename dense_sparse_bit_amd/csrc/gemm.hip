@@ -15,8 +15,9 @@
 //   * every product is a multiple of 2^-18 and a group sum is at most
 //     128 * 49 = 6272 units in magnitude (T = 14 P + Pr at most 15 * 6272), far
 //     below 2^24, so the fp32 MFMA result is the exact integer sum times 2^-18;
-//   * the block rows' CSR lists of chosen residual blocks are walked in step with
-//     g (the "zipper"); a chosen 64-wide block costs one more MFMA per output
+//   * the chosen residual blocks are found in step with g (the "zipper"): from the
+//     dense block map (one coalesced load of a wave's entries) or by walking the
+//     block row's CSR list; a chosen 64-wide block costs one more MFMA per output
 //     tile on the same activation operands, giving Pr exactly;
 //   * each group is dequantized into an fp32 accumulator: acc += s * 2^18 * P,
 //     and for a group with chosen blocks acc += fp32(s / 14) * 2^18 * (14 P + Pr)
@@ -45,13 +46,14 @@ __device__ __forceinline__ void store_out(const GemmArgs& a, int OUTMODE, int m,
 
 // ===========================================================================
 // Decode kernel, M <= 32: one workgroup per 16 output columns, its waves split
-// K into runs of 4-group quads (a quad's four scales are one 8-byte load per
-// lane). Each wave streams its tiles with the next quad's loads (weights,
-// activations, residual rows, scales) in flight while the current quad is
-// multiplied, then the waves' partial tiles are summed through LDS in wave
-// order, so results do not depend on timing. The vector memory pipeline, not
-// HBM, limits this shape class: every load instruction counts, hence 1 KB per
-// instruction for weights and activations and one scale load per quad.
+// K into runs of 4-group quads (16 waves per workgroup on layers of at most 4096
+// columns, else about 2048 waves per launch; see plan_decode). Each wave streams
+// its groups in steps of two (one for the two-row-tile residual variant) with the
+// next step's loads (weights, activations, residual rows, scales) in flight while
+// the current step is multiplied, then the waves' partial tiles are summed through
+// LDS in wave order, so results do not depend on timing. Load latency and the
+// vector memory pipeline, not HBM bytes, limit this shape class: every load
+// instruction counts, hence 1 KB per instruction for weights and activations.
 // ===========================================================================
 constexpr int kMaxDecodeWaves = 16;
 static_assert(kMaxDecodeWaves <= kQaMaxWaves, "the quantizing workgroups run with the decode block size");
