@@ -47,7 +47,11 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 F8_PEAK_TOPS = 5000.0           # MI355X dense fp8 (and int8) MFMA
 ROTATE_BYTES = 640 << 20        # > 2 x (256 MB Infinity Cache + 8 x 4 MB L2)
 GEMM_SRC = os.path.join("dense_sparse_bit_amd", "csrc", "gemm.hip")
-TRAFFIC_SUMMARY = os.path.join("profiles", "gemm_prefill_qwen3_14b_counters.txt")
+# rocprofv3 FETCH_SIZE / WRITE_SIZE summaries per workload, all taken at the 10% budget
+TRAFFIC_SUMMARIES = {w: os.path.join("profiles", f"gemm_{p}_counters.txt") for w, p in (
+    ("qwen3_14b_prefill", "prefill_qwen3_14b"), ("llama3_8b_qo", "decode_llama3_8b_qo"),
+    ("llama3_8b_up_m4", "decode_llama3_8b_up_m4"), ("llama3_8b_down_m4", "decode_llama3_8b_down_m4"))}
+TRAFFIC_BUDGET_PCT = 10
 
 # workloads measured beside the headline in one default run: (config, budgets in %)
 LEGS = [("llama3_8b_qo", (10,)),
@@ -518,34 +522,50 @@ def counters_summary(db_paths, title, commands, only="k_gemm"):
     return "\n".join(out)
 
 
-def traffic_from_profile(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or None when
-    the summary is missing or was taken from different kernel source."""
-    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+def fused_kernel_match(cfg):
+    """(prefix, suffix) that pick the fused GEMM's kernel (residual on, no accumulator
+    dump, output mode 0) out of a kernel list: k_gemm_wide when M > 32, else
+    k_gemm_decode; its tile template arguments sit between the two."""
+    if cfg.M > 32:
+        return "k_gemm_wide<", ", true, false, 0>"
+    return "k_gemm_decode<", ", true, false, 0, false>"
+
+
+def traffic_from_profile(cfg, pct):
+    """(kernel name, HBM bytes per launch) of the fused GEMM's kernel in the committed
+    counter summary of this workload and budget; None for either when there is no such
+    summary, bytes None when it was taken from different kernel source."""
+    path = TRAFFIC_SUMMARIES.get(cfg.name)
+    if path is None or pct != TRAFFIC_BUDGET_PCT:
+        return None, None
+    path = os.path.join(ROOT, path)
     if not os.path.exists(path):
-        return None
+        return None, None
     text = open(path).read()
     if f"sha256: {_src_digest()}" not in text:
-        return None
+        return None, None
     lines = text.splitlines()
+    pre, suf = fused_kernel_match(cfg)
     total, found = 0.0, 0
     for i, l in enumerate(lines):
-        if l.startswith("kernel ") and kernel in l:
+        if l.startswith("kernel ") and pre in l and suf in l:
+            name = l[len("kernel "):].split("(")[0].removeprefix("void ").removeprefix("mq::")
             for l2 in lines[i + 1:]:
                 if l2.startswith("kernel "):
                     break
                 if ("FETCH_SIZE" in l2 or "WRITE_SIZE" in l2) and "MB per dispatch" in l2:
                     total += float(l2.split("->")[1].split()[0]) * 1e6
                     found += 1
-            break
-    return int(total) if found == 2 else None
+            return name, (int(total) if found == 2 else None)
+    return None, None
 
 
 # --------------------------------------------------------------------------- sweep (batch sizes, layer stack)
 def sweep(mq, torch, calls):
     """Fused, dense-only, separate and bf16 matmul at M = 1..256 on the LLaMA3-8B-shaped
     MLP up layer (10%), and a LLaMA3-8B-shaped linear stack (q, k, v, o, gate, up,
-    down; per-layer activation quantization + fused GEMM vs bf16 matmuls) end to end."""
+    down; per-layer activation quantization + fused GEMM, or the self-quantizing GEMM,
+    vs bf16 matmuls) end to end."""
     res = {"batch": [], "stack": []}
     for M in (1, 2, 4, 8, 16, 24, 32, 64, 128, 256):
         cfg = synth.custom_config(f"llama3_8b_up_m{M}", M=M, K=4096, N=14336, bn=64)
@@ -575,6 +595,16 @@ def sweep(mq, torch, calls):
                 mq.gemm_w4a4_residual(lay.xq, lay.sx, p["wq"], p["sw"], p["row_ptr"], p["col_idx"], p["rq"],
                                       lay.cfg.K, bn=64, y=y, rmap=p["rmap"])
 
+        sync = mq.sync_words()
+
+        def ours_act(i):
+            # the same stack through the self-quantizing call (its launch rule picks one
+            # launch or two per layer); the layers run in stream order, so they share one
+            # counter array
+            for lay, p, y, _, _ in layers:
+                mq.gemm_w4a4_residual_act(lay.x, p["wq"], p["sw"], p["rmap"], p["rq"], lay.cfg.K, bn=64, y=y,
+                                          xq=lay.xq, sx=lay.sx, sync=sync)
+
         def dense_only(i):
             for lay, p, y, _, _ in layers:
                 mq.quantize_act(lay.x, xq=lay.xq, sx=lay.sx)
@@ -584,14 +614,16 @@ def sweep(mq, torch, calls):
             for lay, p, y, wb, xb in layers:
                 torch.matmul(xb, wb.t(), out=y)
         t_ours = _graph_time_us(torch, ours, 20)
+        t_act = _graph_time_us(torch, ours_act, 20)
         t_dense = _graph_time_us(torch, dense_only, 20)
         t_bf16 = _graph_time_us(torch, bf16, 20)
-        res["stack"].append({"M": M, "fused_us": round(t_ours, 2), "dense_us": round(t_dense, 2),
+        res["stack"].append({"M": M, "fused_us": round(t_ours, 2), "fused_act_us": round(t_act, 2),
+                             "dense_us": round(t_dense, 2),
                              "bf16_us": round(t_bf16, 2), "speedup_vs_bf16": round(t_bf16 / t_ours, 3),
                              "overhead_vs_dense": round(t_ours / t_dense - 1, 4),
                              "note": "weights of each layer read once per pass (7 layers, 218 MB of "
                                      "bf16 weights; the Infinity Cache can hold part of the packed ones)"})
-        log(f"[sweep] stack M={M}: fused {t_ours:.1f} dense {t_dense:.1f} bf16 {t_bf16:.1f} us")
+        log(f"[sweep] stack M={M}: fused {t_ours:.1f} act {t_act:.1f} dense {t_dense:.1f} bf16 {t_bf16:.1f} us")
         del layers
         torch.cuda.empty_cache()
     return res
@@ -693,7 +725,9 @@ def main():
         achieved, peak, unit = ops / st["gemm_us"] / 1e6, F8_PEAK_TOPS, "TOPS"
     else:
         achieved, peak, unit = gemm_bytes(cfg, k_blocks) / st["gemm_us"] / 1e3, HBM_PEAK_GBS, "GB/s"
-    kname = "k_gemm_wide<4, true, false, 0>" if cfg.M > 32 else "k_gemm_decode"
+    kname, traffic = traffic_from_profile(cfg, pct)
+    if kname is None:
+        kname = fused_kernel_match(cfg)[0] + "...>"
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -719,10 +753,10 @@ def main():
                    "k_blocks": k_blocks, "step": "quantize_act -> gemm_w4a4_residual"},
         "roofline": {"kernel": kname, "bound": kind, "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": traffic_from_profile("k_gemm_wide<4, true, false" if cfg.M > 32 else "k_gemm_decode<"),
+                     "traffic": traffic,
                      "per_launch": {"ops": ops, "bytes": gemm_bytes(cfg, k_blocks), "us": round(st["gemm_us"], 3)},
                      "hbm_GBs": round(gemm_bytes(cfg, k_blocks) / st["gemm_us"] / 1e3, 1),
-                     "traffic_source": TRAFFIC_SUMMARY + " (rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled "
+                     "traffic_source": TRAFFIC_SUMMARIES.get(cfg.name, "none for this workload") + " (rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled "
                                        "by a copy of known size; null when the kernel source changed since)"},
         "step_kernels_us": {"quantize_act": round(st["quant_us"], 3), "gemm_w4a4_residual": round(st["gemm_us"], 3)},
         "gemm": gemm,

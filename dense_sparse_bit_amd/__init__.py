@@ -431,8 +431,8 @@ _ACT_LAUNCH = {"auto": 0, "one": 1, "two": 2}   # MQ_ACT_AUTO, MQ_ACT_ONE_LAUNCH
 
 def act_one_launch(M: int, N: int, K: int, launch: str = "auto") -> bool:
     """Whether gemm_w4a4_residual_act runs as one launch (the library's own rule for
-    "auto": M <= 32 and M N <= 12 K)."""
-    return launch == "one" or (launch == "auto" and M <= 32 and M * N <= 12 * K)
+    "auto": M <= 32, N <= 5120, and M <= 4 or K >= 12288)."""
+    return launch == "one" or (launch == "auto" and M <= 32 and N <= 5120 and (M <= 4 or K >= 12288))
 
 
 def gemm_w4a4_residual_act(x, wq, sw, rmap, rq, K: int, bn: int = 64, out_dtype=torch.bfloat16, y=None,

@@ -280,11 +280,14 @@ int mq_gemm_w4a4_residual_act(const void* x, int x_dtype, const uint8_t* wq, con
         return MQ_ERR_INVALID_ARG;
     if (nnz * bn * (bk / 2) > (int64_t(1) << 31)) return MQ_ERR_UNSUPPORTED;
     if (launch == MQ_ACT_ONE_LAUNCH && M > 32) return MQ_ERR_INVALID_ARG;
-    // measured crossover on MI355X: the one-launch form's wait grows with the
-    // tokens and the column workgroups (M N), the stand-alone quantization with the
-    // row length (K); one launch measured faster up to M N / K = 9.1 and slower
-    // from 14 on, so the rule splits at 12
-    const bool one = launch == MQ_ACT_ONE_LAUNCH || (launch == MQ_ACT_AUTO && M <= 32 && M * N <= 12 * K);
+    // measured crossover on MI355X (K x N from 4096 x 1024 to 28672 x 8192, M = 1..32):
+    // the one-launch form quantizes each token in one workgroup of the decode plan's
+    // waves, and past N = 5120 the plan gives at most 4 waves per workgroup, which
+    // quantize a row far slower than the stand-alone kernel (two launches faster at
+    // every M measured); up to N = 5120 one launch hides a long quantization
+    // (K >= 12288: faster at every M) and otherwise wins only at M <= 4
+    const bool one = launch == MQ_ACT_ONE_LAUNCH ||
+                     (launch == MQ_ACT_AUTO && M <= 32 && N <= 5120 && (M <= 4 || K >= 12288));
     if (M == 0) return MQ_OK;
     if (!x || !aligned16(x) || (one && (!sync || (reinterpret_cast<uintptr_t>(sync) & 3u))))
         return MQ_ERR_INVALID_ARG;

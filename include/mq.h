@@ -245,8 +245,9 @@ int mq_gemm_w4a4_residual_mapped(const uint8_t* xq, const float* sx, const uint8
  * `sync`) before reading any activation; or as two launches on `stream`,
  * mq_quantize_act and then the GEMM. `launch` picks: MQ_ACT_ONE_LAUNCH (M > 32
  * is then an invalid argument), MQ_ACT_TWO_LAUNCHES, or MQ_ACT_AUTO, which takes
- * one launch when M <= 32 and M N <= 12 K (where it measured faster on MI355X: a
- * few long rows over few columns) and two otherwise. Both give the same bits.
+ * one launch when M <= 32, N <= 5120 and either M <= 4 or K >= 12288 (where it
+ * measured faster on MI355X: few output columns, and few tokens or long rows) and
+ * two otherwise. Both give the same bits.
  * x: [M][K] fp32 or bf16 (x_dtype), 16-byte aligned; xq, sx: outputs as in
  * mq_quantize_act; rmap, rq, nnz: as in mq_gemm_w4a4_residual_mapped (rmap required).
  * sync (required when the one-launch form runs, else unused and may be null):
