@@ -16,7 +16,8 @@
 //     128 * 49 = 6272 units in magnitude (T = 14 P + Pr at most 15 * 6272), far
 //     below 2^24, so the fp32 MFMA result is the exact integer sum times 2^-18;
 //   * the chosen residual blocks are found in step with g (the "zipper"): from the
-//     dense block map (one coalesced load of a wave's entries) or by walking the
+//     dense block map (one coalesced load of a wave's entries, issued ahead of
+//     its operand loads in the decode kernel) or by walking the
 //     block row's CSR list; a chosen 64-wide block costs one more MFMA per output
 //     tile on the same activation operands, giving Pr exactly;
 //   * each group is dequantized into an fp32 accumulator: acc += s * 2^18 * P,
@@ -305,32 +306,41 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
     // two steps in flight: step i+1 is fetched while step i is multiplied
     // (ping-pong buffers, so no register copy waits on the prefetch)
     DecStep<MT, QS> s0, s1;
-    if (gb < ge) dec_fetch_main<MT, QS, !QX>(s0, src, gb, lane);
-    if (RES) {
+    if (gb < ge) {
         // The zipper table of this wave's column blocks [2 gb, 2 ge), built by the
-        // wave alone while its first loads are in flight: no workgroup barrier.
-        // A wavefront's LDS operations complete in issue order, so the -1 fill,
-        // the CSR positions and the later reads need no wait between lanes.
-        // With a block map the table is one coalesced load of the wave's entries
-        // (out-of-range positions read as "no block"); no dependent loads.
+        // wave alone: no workgroup barrier. A wavefront's LDS operations complete in
+        // issue order, so the fills and the later reads need no wait between lanes.
+        // With a block map the wave's first 64 entries are requested before its
+        // operands: loads return in issue order, so the table (and the residual
+        // fetch that needs it) waits for that one load, not for the operands. The
+        // index is clamped into the wave's range, so every lane loads a map entry.
+        // (Everything stays inside this branch: a load left in flight across the
+        // join would make the compiler drain every load before reusing its register.)
         const int kb0 = 2 * gb, kb1 = 2 * ge;
-        for (int i = kb0 + lane; i < kb1; i += 64) {
-            int v = -1;
+        int map0 = -1;
+        if (RES && map) map0 = a.rmap[static_cast<int64_t>(br) * (2 * G) + min(kb0 + lane, kb1 - 1)];
+        dec_fetch_main<MT, QS, !QX>(s0, src, gb, lane);
+        if (RES) {
             if (map) {
-                v = a.rmap[static_cast<int64_t>(br) * (2 * G) + i];
-                v = (v >= 0 && v < a.nnz) ? v : -1;
+                // out-of-range positions read as "no block"
+                if (kb0 + lane < kb1) tab[kb0 + lane] = (map0 >= 0 && map0 < a.nnz) ? map0 : -1;
+                for (int i = kb0 + lane + 64; i < kb1; i += 64) {
+                    const int v = a.rmap[static_cast<int64_t>(br) * (2 * G) + i];
+                    tab[i] = (v >= 0 && v < a.nnz) ? v : -1;
+                }
+                __builtin_amdgcn_wave_barrier();
+            } else {
+                // from the block row's CSR list: -1 everywhere, then the positions
+                for (int i = kb0 + lane; i < kb1; i += 64) tab[i] = -1;
+                __builtin_amdgcn_wave_barrier();
+                for (int i = lo + lane; i < hi; i += 64) {
+                    const int kb = a.col_idx[i];
+                    if (kb >= kb0 && kb < kb1) tab[kb] = i;
+                }
+                __builtin_amdgcn_wave_barrier();
             }
-            tab[i] = v;
+            dec_fetch_res<MT, QS, RES>(s0, a, src, tab, rrow, G, gb, lane);
         }
-        __builtin_amdgcn_wave_barrier();
-        if (!map) {
-            for (int i = lo + lane; i < hi; i += 64) {
-                const int kb = a.col_idx[i];
-                if (kb >= kb0 && kb < kb1) tab[kb] = i;
-            }
-            __builtin_amdgcn_wave_barrier();
-        }
-        if (gb < ge) dec_fetch_res<MT, QS, RES>(s0, a, src, tab, rrow, G, gb, lane);
     }
     const int C = QX ? static_cast<int>(gridDim.x) - a.M : 0;   // column workgroups
     if (QX) {
