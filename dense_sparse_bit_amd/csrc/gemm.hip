@@ -15,14 +15,16 @@
 //   * every product is a multiple of 2^-18 and a group sum is at most
 //     128 * 49 = 6272 units in magnitude (T = 14 P + Pr at most 15 * 6272), far
 //     below 2^24, so the fp32 MFMA result is the exact integer sum times 2^-18;
-//   * the chosen residual blocks are found in step with g (the "zipper"): from the
-//     dense block map (one coalesced load of a wave's entries, issued ahead of
-//     its operand loads in the decode kernel) or by walking the
-//     block row's CSR list; a chosen 64-wide block costs one more MFMA per output
-//     tile on the same activation operands, giving Pr exactly;
+//   * the chosen residual blocks are found from the dense block map (one
+//     coalesced load of a wave's entries, issued ahead of its operand loads in
+//     the decode kernel) or by walking the block row's CSR list; a chosen 64-wide
+//     block costs one more MFMA per output tile, giving Pr exactly. The decode
+//     kernel walks them in step with g (the "zipper"), on the same activation
+//     operands; the prefill kernel multiplies them after all groups;
 //   * each group is dequantized into an fp32 accumulator: acc += s * 2^18 * P,
 //     and for a group with chosen blocks acc += fp32(s / 14) * 2^18 * (14 P + Pr)
-//     (decode kernel) or acc += s * 2^18 * P + fp32(s / 14) * 2^18 * Pr (prefill);
+//     (decode kernel); the prefill kernel adds acc += fp32(s / 14) * 2^18 * Pr per
+//     chosen block once every group's dense part is in;
 //   * the epilogue multiplies by the token scale sx and stores bf16 (RNE) or fp32.
 // The debug build (acc_dump) writes every group's exact T = 14 P + Pr.
 #include <algorithm>
@@ -459,8 +461,9 @@ __device__ __forceinline__ int xcd_tile(int b, int T) {
 
 // ===========================================================================
 // Wide prefill kernel, M > 32: a workgroup of NWN waves owns 96 tokens x 64 NWN
-// output columns, and each wave all 96 tokens of its own 64 columns (3 x 2 tiles
-// of 32 x 32, 32 x 32 x 64 fp8 MFMAs), one 128-wide K group per step.
+// output columns (32 x 64 NWN for the mid-size tile), and each wave all of its
+// tokens for its own 64 columns (3 x 2 tiles of 32 x 32, 32 x 32 x 64 fp8 MFMAs),
+// one 128-wide K group per step.
 //   * Every weight tile is loaded and widened to fp8 by exactly one wave (straight
 //     from memory into registers, a group ahead of its use).
 //   * Every activation tile is loaded and widened once per workgroup: the waves
@@ -469,12 +472,12 @@ __device__ __forceinline__ int xcd_tile(int b, int T) {
 //     One barrier per group.
 //   * Per group and tile: P from two MFMAs (one per 64-input half), then
 //     acc += fp32(s) * 2^18 * P.
-//   * A half of a group holding a chosen block of the wave's block row (a scalar
-//     branch: a wave's 64 columns lie in one block row) adds one MFMA per tile on
-//     that half's activation operands, acc += fp32(s / 14) * 2^18 * Pr. The block's
-//     codes are fetched during the group's step and multiplied at the start of the
-//     next one, so their latency is hidden; LDS therefore keeps three stages of
-//     activation operands (the group being finished, the current one, the next).
+//   * The chosen blocks of the wave's block row (a wave's 64 columns lie in one
+//     block row) are multiplied after the last group, one MFMA per tile on
+//     activations the wave loads and widens itself: acc += fp32(s / 14) * 2^18 * Pr.
+//     Done inside the K loop, they made every wave wait at each group's barrier for
+//     the wave with the most chosen blocks in that group (the waves of a workgroup
+//     cover several block rows); after it, that imbalance costs once per tile.
 // Per group and wave the VALU work is the 96 dequantizing FMAs, the widening of
 // 4 KB of weight nibbles and 1/NWN of the activation widening, against 12 MFMAs:
 // close to balanced, so two waves per SIMD keep the MFMA pipe fed. 96 rows (not
@@ -486,11 +489,6 @@ constexpr int kMidMaxM = 384;       // measured on the LLaMA3-8B MLP up layer: t
                                     // tile 2.3x faster at M = 64, 1.5x at 384, equal at 512
 constexpr int kMidWaves = 2;
 
-struct WideRes {
-    uint4 r[2];        // codes of the first chosen half [column tile j] (zeros if none)
-    int rmask;         // bit h: half h holds a chosen block (wave-uniform)
-    int jb1;           // CSR position of half 1's block, or -1
-};
 
 template <int NWN, int MTW, bool RES, bool DUMP, int OUTMODE>
 __global__ __launch_bounds__(64 * NWN, DUMP ? 1 : 2) void k_gemm_wide(GemmArgs a, int n_begin, int tiles_n) {
@@ -498,7 +496,7 @@ __global__ __launch_bounds__(64 * NWN, DUMP ? 1 : 2) void k_gemm_wide(GemmArgs a
     constexpr int kWM = 32 * kMT;       // tokens per workgroup tile
     constexpr int kRuns = kWM / 16;                   // 1 KB activation runs per group
     constexpr int kXU = (kRuns + NWN - 1) / NWN;      // runs per wave (run wave + NWN u)
-    constexpr int kStages = RES ? 3 : 2;
+    constexpr int kStages = 2;
     // [stage][32-row tile][half 2][part 2][lane 64][16 B]
     __shared__ __align__(16) uint8_t xs[kStages][kMT][2][2][1024];
     __shared__ __align__(16) uint8_t xspare[(kXU * NWN > kRuns) ? 2048 : 16];
@@ -668,25 +666,52 @@ __global__ __launch_bounds__(64 * NWN, DUMP ? 1 : 2) void k_gemm_wide(GemmArgs a
             }
         }
     };
-    // the chosen halves of group g and the first one's codes (an absent block reads
-    // zeros: the load is issued every step, so no register copy waits on it)
-    auto load_res = [&](int g, WideRes& R) __attribute__((always_inline)) {
-        const int jb0 = __builtin_amdgcn_readfirstlane(wt[2 * g]);
-        const int jb1 = __builtin_amdgcn_readfirstlane(wt[2 * g + 1]);
-        R.rmask = (jb0 >= 0 ? 1 : 0) | (jb1 >= 0 ? 2 : 0);
-        R.jb1 = jb1;
-        const int jb = jb0 >= 0 ? jb0 : jb1;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) R.r[j] = load_codes(jb, j);
+    // Residual blocks, after every group's dense part: the wave's chosen blocks (its
+    // 64 columns lie in one block row), each one MFMA per 32 x 32 tile on
+    // activations the wave loads itself (16 bytes per lane and row tile, from L2)
+    // and widens: acc += fp32(s / 14) * 2^18 * Pr. No barrier follows, so a wave
+    // with more chosen blocks than the others delays no one. A chosen entry is
+    // packed as (CSR position - wlo) << 11 | column block: a list position is below
+    // the block row's 2 G column blocks, a map position below 2^20 (the payload
+    // offset check), a column block below 2^11.
+    struct TailOps {
+        uint32_t s[2];      // fp16 group scale bits, column tiles 0 and 1
+        uint4 c[2];         // residual codes, column tiles 0 and 1
+        uint4 x[kMT];       // activation codes, row tiles
+        int kb;             // column block
     };
-    // residual pass of half h of group g (stage st): one MFMA per tile
-    auto res_half = [&](int g, int st, int h, const uint4 (&codes)[2], const float (&fr)[2]) __attribute__((always_inline)) {
+    // the activation codes of row tile i, half h of group g for this lane's operand
+    // slot: row m0 + 32 i + lc (rows past M read zero), 16-byte chunk 2 h + lh
+    auto load_res_x = [&](int g, int h, int i) __attribute__((always_inline)) {
+        const int r0 = m0 + 32 * i;
+        const __amdgpu_buffer_rsrc_t rx = buf_rsrc_uniform(
+            a.xq + (static_cast<int64_t>(g) * a.M + r0) * 64, static_cast<uint32_t>(max(0, min(32, a.M - r0))) * 64u);
+        return buf_load16(rx, static_cast<uint32_t>(lc * 64 + (2 * h + lh) * 16));
+    };
+    // e: (CSR position - wlo) << 11 | column block
+    auto tail_fetch = [&](int e, TailOps& T) __attribute__((always_inline)) {
+        const int kb = e & 2047, jb = wlo + (e >> 11), g = kb >> 1, h = kb & 1;
+        T.kb = kb;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            T.s[j] = load_scale(g, j);
+            T.c[j] = load_codes(jb, j);
+        }
+#pragma unroll
+        for (int i = 0; i < kMT; ++i) T.x[i] = load_res_x(g, h, i);
+    };
+    auto tail_mul = [&](const TailOps& T) __attribute__((always_inline)) {
+        const int g = T.kb >> 1;
+        float fr[2];
         v8i ra[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) ra[j] = f8_operand(codes[j]);
+        for (int j = 0; j < 2; ++j) {
+            fr[j] = div14(f16_bits_to_f32(static_cast<uint16_t>(T.s[j]))) * kF8Unit;
+            ra[j] = f8_operand(T.c[j]);
+        }
 #pragma unroll
         for (int i = 0; i < kMT; ++i) {
-            const v8i aa = a_operand(st, i, h);
+            const v8i aa = f8_operand(T.x[i]);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const v16f z = {};
@@ -706,18 +731,74 @@ __global__ __launch_bounds__(64 * NWN, DUMP ? 1 : 2) void k_gemm_wide(GemmArgs a
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // residual pass of group g: the first chosen half's codes were fetched a step
-    // earlier; a second chosen half (rare) is fetched and used here
-    auto residual = [&](int g, int st, const WideRes& R, const uint32_t (&sb)[2]) __attribute__((always_inline)) {
-        float fr[2];
+    auto residual_blocks = [&]() __attribute__((always_inline)) {
+        if constexpr (kMT == 1) {
+            // one row tile: the table is compacted in place into the list of chosen
+            // entries (every lane reads its entry of a 64-entry chunk before any lane
+            // writes, and an entry moves only to an index no later than its own), which
+            // is walked with the next block's operands fetched while one is multiplied
+            int n = 0;
+            for (int c0 = 0; c0 < nbc; c0 += 64) {
+                const int v = c0 + lane < nbc ? wt[c0 + lane] : -1;
+                const uint64_t chosen = __ballot(v >= 0);
+                __builtin_amdgcn_wave_barrier();
+                if (v >= 0) {
+                    const int below = __builtin_popcountll(chosen & ((uint64_t(1) << lane) - 1));
+                    wt[n + below] = ((v - wlo) << 11) | (c0 + lane);
+                }
+                __builtin_amdgcn_wave_barrier();
+                n += __builtin_popcountll(chosen);
+            }
+            TailOps t0, t1;
+            if (n > 0) tail_fetch(__builtin_amdgcn_readfirstlane(wt[0]), t0);
+            for (int q = 0; q < n; q += 2) {
+                if (q + 1 < n) tail_fetch(__builtin_amdgcn_readfirstlane(wt[q + 1]), t1);
+                tail_mul(t0);
+                if (q + 1 >= n) break;
+                if (q + 2 < n) tail_fetch(__builtin_amdgcn_readfirstlane(wt[q + 2]), t0);
+                tail_mul(t1);
+            }
+        } else {
+            // three row tiles: a second set of operands in flight spills (measured
+            // slower), and so did fetching all of a block's operands before its
+            // products (210.3 against 206.3 us on the Qwen3-14B prefill shape): the
+            // scales and codes go first, each row tile's activations just before its
+            // MFMAs; the chosen entries of each 64-entry chunk come from one ballot
+            for (int c0 = 0; c0 < nbc; c0 += 64) {
+                const int v = c0 + lane < nbc ? wt[c0 + lane] : -1;
+                uint64_t chosen = __ballot(v >= 0);
+                while (chosen) {
+                    const int bit = __builtin_ctzll(chosen);
+                    chosen &= chosen - 1;
+                    const int jb = __builtin_amdgcn_readlane(v, bit);
+                    const int kb = c0 + bit, g = kb >> 1, h = kb & 1;
+                    float fr[2];
+                    v8i ra[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) fr[j] = div14(f16_bits_to_f32(static_cast<uint16_t>(sb[j]))) * kF8Unit;
-        res_half(g, st, (R.rmask & 1) ? 0 : 1, R.r, fr);
-        if (R.rmask == 3) {
-            uint4 c[2];
+                    for (int j = 0; j < 2; ++j) {
+                        fr[j] = div14(f16_bits_to_f32(static_cast<uint16_t>(load_scale(g, j)))) * kF8Unit;
+                        ra[j] = f8_operand(load_codes(jb, j));
+                    }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) c[j] = load_codes(R.jb1, j);
-            res_half(g, st, 1, c, fr);
+                    for (int i = 0; i < kMT; ++i) {
+                        const v8i aa = f8_operand(load_res_x(g, h, i));
+#pragma unroll
+                        for (int j = 0; j < 2; ++j) {
+                            const v16f z = {};
+                            const v16f pr = mfma32_f8(aa, ra[j], z);
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(fr[j], pr[r], acc[i][j][r]);
+                            if (DUMP) {
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) {
+                                    const int64_t d = dump_idx(i, j, r, g);
+                                    if (d >= 0) a.acc_dump[d] += static_cast<int>(pr[r] * kF8Unit);
+                                }
+                            }
+                        }
+                    }
+                }
+            }
         }
     };
 
@@ -750,17 +831,13 @@ __global__ __launch_bounds__(64 * NWN, DUMP ? 1 : 2) void k_gemm_wide(GemmArgs a
         __builtin_amdgcn_sched_group_barrier(0x0020, kXU, 0);     // loads of group g + 2
     };
 
-    // Pipeline: step g (stage g % kStages) first finishes group g - 1's residual
-    // pass (its codes were fetched during step g - 1), then fetches group g + 2's
-    // weights and scales and group g's residual codes, multiplies group g with the
-    // weights fetched during step g - 2, widens group g + 1's activations (fetched
-    // during step g - 1) into the next stage and fetches group g + 2's. Unrolled by
-    // three so that the weight and scale registers rotate without copies.
+    // Pipeline: step g (stage g % kStages) fetches group g + 2's weights and scales,
+    // multiplies group g with the weights fetched during step g - 2, widens group
+    // g + 1's activations (fetched during step g - 1) into the other stage and
+    // fetches group g + 2's. Unrolled by three so that the weight and scale
+    // registers rotate without copies.
     uint4 B0[2][2], B1[2][2], B2[2][2], X[kXU];
     uint32_t S0[2], S1[2], S2[2];
-    WideRes R;
-    R.rmask = 0;
-    R.jb1 = -1;
     load_x(0, X);
     load_w(0, B0);
     load_w(1, B1);
@@ -777,20 +854,14 @@ __global__ __launch_bounds__(64 * NWN, DUMP ? 1 : 2) void k_gemm_wide(GemmArgs a
     auto step = [&](int g, const uint4 (&Bc)[2][2], uint4 (&Bn)[2][2], const uint32_t (&Sc)[2],
                     uint32_t (&Sn)[2]) __attribute__((always_inline)) {
         const int st = g % kStages;
-        // Each SIMD runs two of these waves. While one issues its MFMAs (the previous
-        // group's residual and this group's base products) it takes issue priority
-        // over the other, which is then in its loads, widening or barrier: the MFMA
-        // pipe idles less (measured: fused 219 -> 214 us, dense 190 -> 179 us on the
+        // Each SIMD runs two of these waves. While one issues its MFMAs it takes
+        // issue priority over the other, which is then in its loads, widening or
+        // barrier: the MFMA pipe idles less (measured: dense 190 -> 179 us on the
         // Qwen3-14B prefill shape).
         __builtin_amdgcn_s_setprio(1);
-        if (RES && R.rmask) {
-            __asm__ volatile("" ::: "memory");
-            residual(g - 1, (g + kStages - 1) % kStages, R, Sn);   // Sn still holds group g - 1's scales
-        }
         load_w(g + 2, Bn);
 #pragma unroll
         for (int j = 0; j < 2; ++j) Sn[j] = load_scale(g + 2, j);
-        if (RES) load_res(g, R);
         compute(g, st, Bc, Sc);
         __builtin_amdgcn_s_setprio(0);
         store_x(X, (g + 1) % kStages);
@@ -805,7 +876,7 @@ __global__ __launch_bounds__(64 * NWN, DUMP ? 1 : 2) void k_gemm_wide(GemmArgs a
         if (g + 2 >= G) break;
         step(g + 2, B2, B1, S2, S1);
     }
-    if (RES && R.rmask) residual(G - 1, (G - 1) % kStages, R, (G - 1) % 3 == 0 ? S0 : ((G - 1) % 3 == 1 ? S1 : S2));
+    if (RES) residual_blocks();
 
     // Epilogue: y = acc * sx, bf16 or fp32 (rows past M and columns past N skipped)
     const __amdgpu_buffer_rsrc_t rsx = buf_rsrc_uniform(a.sx + m0, static_cast<uint32_t>(max(0, min(kWM, a.M - m0))) * 4u);
@@ -898,11 +969,10 @@ static hipError_t go_decode(const GemmArgs& a, hipStream_t st) {
 
 template <bool RES, bool DUMP, int OUT>
 static hipError_t go_wide(const GemmArgs& a, hipStream_t st) {
-    // the fused kernel: eight waves (512 columns) share each group's activation
-    // widening and fetch (measured 214.5 -> 210.7 us on the Qwen3-14B prefill
-    // shape); the dense-only kernel spills at eight and keeps four. Every output is
-    // summed by one wave in group order either way, so the two agree bit for bit
-    // on an empty residual.
+    // four waves (256 columns) per workgroup for both kernels (at eight the
+    // dense-only loop, which the fused kernel now shares, measured 193.7 against
+    // 179.7 us on the Qwen3-14B prefill shape). Every output is summed by one wave
+    // in group order in both, so they agree bit for bit on an empty residual.
     if (a.M <= kMidMaxM) {
         // 32 < M <= 384: one 32-row tile per wave and two waves (128 columns) per
         // workgroup, so that the grid has enough workgroups (96 x 512 tiles give 28
@@ -913,7 +983,7 @@ static hipError_t go_wide(const GemmArgs& a, hipStream_t st) {
         k_gemm_wide<NWN, MTW, RES, DUMP, OUT><<<dim3(tiles), dim3(64 * NWN), 0, st>>>(a, 0, tiles_n);
         return hipGetLastError();
     }
-    constexpr int NWN = RES ? 8 : 4, MTW = kWideRowTiles;
+    constexpr int NWN = 4, MTW = kWideRowTiles;
     const int tiles_n = (a.N + 64 * NWN - 1) / (64 * NWN);
     const int tiles = ((a.M + 32 * MTW - 1) / (32 * MTW)) * tiles_n;
     k_gemm_wide<NWN, MTW, RES, DUMP, OUT><<<dim3(tiles), dim3(64 * NWN), 0, st>>>(a, 0, tiles_n);
