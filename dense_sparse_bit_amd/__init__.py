@@ -45,6 +45,7 @@ _SIGS = {
     "mq_gemm_w4a4_dense": [_p, _p, _p, _p, _i64, _i64, _i64, _int, _p, _int, _p, _p],
     "mq_block_map": [_p, _p, _i64, _i64, _i64, _int, _int, _p, _p],
     "mq_read_probe": [_p, _i64, _p, _p],
+    "mq_act_one_launch": [_i64, _i64, _i64],
     "mq_gemm_w4a4_residual_act": [_p, _int, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
                                   _p, _p, _p, _int, _p, _int, _p],
     "mq_gemm_w4a4_residual_mapped": [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _int, _int, _int,
@@ -430,9 +431,9 @@ _ACT_LAUNCH = {"auto": 0, "one": 1, "two": 2}   # MQ_ACT_AUTO, MQ_ACT_ONE_LAUNCH
 
 
 def act_one_launch(M: int, N: int, K: int, launch: str = "auto") -> bool:
-    """Whether gemm_w4a4_residual_act runs as one launch (the library's own rule for
-    "auto": M <= 32, N <= 5120, and M <= 4 or K >= 12288)."""
-    return launch == "one" or (launch == "auto" and M <= 32 and N <= 5120 and (M <= 4 or K >= 12288))
+    """Whether gemm_w4a4_residual_act runs as one launch ("auto": the library's own
+    rule, mq_act_one_launch)."""
+    return launch == "one" or (launch == "auto" and _lib.mq_act_one_launch(M, N, K) == 1)
 
 
 def gemm_w4a4_residual_act(x, wq, sw, rmap, rq, K: int, bn: int = 64, out_dtype=torch.bfloat16, y=None,

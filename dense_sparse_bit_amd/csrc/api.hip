@@ -267,6 +267,22 @@ int mq_gemm_w4a4_residual_mapped(const uint8_t* xq, const float* sx, const uint8
 
 static_assert(mq::kSyncWords == MQ_SYNC_WORDS, "sync array size");
 
+
+// Measured crossover on MI355X (K x N from 4096 x 1024 to 28672 x 8192, M = 1..32).
+// The one-launch form quantizes each token in one workgroup of the decode plan's
+// nw waves; where that is narrower than the stand-alone quantizer's workgroup, its
+// tokens take longer and two launches were faster at every M measured. Otherwise
+// one launch saves the second launch and hides the quantization behind the first
+// weight loads: it was faster for one token, and for up to 16 tokens of rows of
+// at least 12288 inputs, and slower (or level) at more tokens.
+int mq_act_one_launch(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || M > 32 || N < 16 || K < mq::kGroup) return 0;
+    if (64 * mq::plan_decode(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K)).nw <
+        mq::quant_act_threads(M, K))
+        return 0;
+    return (M == 1 || (M <= 16 && K >= 12288)) ? 1 : 0;
+}
+
 int mq_gemm_w4a4_residual_act(const void* x, int x_dtype, const uint8_t* wq, const uint16_t* sw,
                               const int32_t* rmap, const uint8_t* rq, int64_t nnz, int64_t M, int64_t N,
                               int64_t K, int group, int bn, int bk, uint8_t* xq, float* sx, int32_t* sync,
@@ -280,14 +296,7 @@ int mq_gemm_w4a4_residual_act(const void* x, int x_dtype, const uint8_t* wq, con
         return MQ_ERR_INVALID_ARG;
     if (nnz * bn * (bk / 2) > (int64_t(1) << 31)) return MQ_ERR_UNSUPPORTED;
     if (launch == MQ_ACT_ONE_LAUNCH && M > 32) return MQ_ERR_INVALID_ARG;
-    // measured crossover on MI355X (K x N from 4096 x 1024 to 28672 x 8192, M = 1..32):
-    // the one-launch form quantizes each token in one workgroup of the decode plan's
-    // waves, and past N = 5120 the plan gives at most 4 waves per workgroup, which
-    // quantize a row far slower than the stand-alone kernel (two launches faster at
-    // every M measured); up to N = 5120 one launch hides a long quantization
-    // (K >= 12288: faster at every M) and otherwise wins only at M <= 4
-    const bool one = launch == MQ_ACT_ONE_LAUNCH ||
-                     (launch == MQ_ACT_AUTO && M <= 32 && N <= 5120 && (M <= 4 || K >= 12288));
+    const bool one = launch == MQ_ACT_ONE_LAUNCH || (launch == MQ_ACT_AUTO && mq_act_one_launch(M, N, K));
     if (M == 0) return MQ_OK;
     if (!x || !aligned16(x) || (one && (!sync || (reinterpret_cast<uintptr_t>(sync) & 3u))))
         return MQ_ERR_INVALID_ARG;

@@ -53,6 +53,8 @@ inline size_t select_scratch_bytes(int64_t nb, bool scores) {
 // activations x^ = fp32(x * r_k)), or null
 hipError_t launch_hessian(const void* x, int bf16, int64_t M, int64_t K, const float* colscale, float* h,
                           hipStream_t st);
+// threads per token of the stand-alone activation quantizer
+int quant_act_threads(int64_t M, int64_t K);
 hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, const float* colscale, uint8_t* xq,
                             float* sx, hipStream_t st);
 hipError_t launch_smooth(const void* x, int bf16, int64_t M, int64_t K, const float* w, int64_t N, float* s,

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void k_hessian(const void* __restrict__ x, int
 // is quant_act_row in mq_quant.h, shared with the GEMM that quantizes its own
 // activations).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_quant_act(const void* __restrict__ x, int bf16, int64_t M, int64_t K,
+__global__ __launch_bounds__(64 * kQaMaxWaves) void k_quant_act(const void* __restrict__ x, int bf16, int64_t M, int64_t K,
                                                    const float* __restrict__ colscale,
                                                    uint8_t* __restrict__ xq, float* __restrict__ sx) {
     __shared__ float red[kQaMaxWaves];
@@ -486,9 +486,25 @@ hipError_t launch_hessian(const void* x, int bf16, int64_t M, int64_t K, const f
     return hipGetLastError();
 }
 
+// Threads per token. Few tokens (M <= 256): enough to hold the whole row in
+// registers (kQaWords words of 8 inputs each), at least 256 and at most 1024, so
+// that each thread's chain of loads is short. Many tokens: 256 (the grid alone
+// fills the chip, and wider workgroups only cost). Measured on MI355X (us per
+// call at 128 / 256 / 512 / 1024 threads): M=16, K=4096 3.80 / 3.46 / 3.46 / 4.50;
+// M=32, K=14336 12.13 / 7.00 / 5.10 / 5.26; M=2048, K=5120 8.70 / 8.95 / 13.22 /
+// 25.59. The width does not change the result: every thread's words are the same
+// whichever of them it holds in registers.
+int quant_act_threads(int64_t M, int64_t K) {
+    if (M > 256) return 256;
+    const int64_t words = K / 8;
+    const int64_t nt = ((words + kQaWords - 1) / kQaWords + 63) / 64 * 64;
+    return static_cast<int>(std::min<int64_t>(64 * kQaMaxWaves, std::max<int64_t>(256, nt)));
+}
+
 hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, const float* colscale, uint8_t* xq,
                             float* sx, hipStream_t st) {
-    k_quant_act<<<dim3(static_cast<unsigned>(M)), dim3(256), 0, st>>>(x, bf16, M, K, colscale, xq, sx);
+    k_quant_act<<<dim3(static_cast<unsigned>(M)), dim3(quant_act_threads(M, K)), 0, st>>>(x, bf16, M, K, colscale,
+                                                                                      xq, sx);
     return hipGetLastError();
 }
 

@@ -245,9 +245,8 @@ int mq_gemm_w4a4_residual_mapped(const uint8_t* xq, const float* sx, const uint8
  * `sync`) before reading any activation; or as two launches on `stream`,
  * mq_quantize_act and then the GEMM. `launch` picks: MQ_ACT_ONE_LAUNCH (M > 32
  * is then an invalid argument), MQ_ACT_TWO_LAUNCHES, or MQ_ACT_AUTO, which takes
- * one launch when M <= 32, N <= 5120 and either M <= 4 or K >= 12288 (where it
- * measured faster on MI355X: few output columns, and few tokens or long rows) and
- * two otherwise. Both give the same bits.
+ * one launch when mq_act_one_launch(M, N, K) says so and two otherwise. Both give
+ * the same bits.
  * x: [M][K] fp32 or bf16 (x_dtype), 16-byte aligned; xq, sx: outputs as in
  * mq_quantize_act; rmap, rq, nnz: as in mq_gemm_w4a4_residual_mapped (rmap required).
  * sync (required when the one-launch form runs, else unused and may be null):
@@ -264,6 +263,15 @@ int mq_gemm_w4a4_residual_mapped(const uint8_t* xq, const float* sx, const uint8
 #define MQ_ACT_AUTO 0
 #define MQ_ACT_ONE_LAUNCH 1
 #define MQ_ACT_TWO_LAUNCHES 2
+/*
+ * The MQ_ACT_AUTO rule of mq_gemm_w4a4_residual_act, for callers that need to know
+ * beforehand whether the counters are required: 1 if the call takes one launch
+ * for this shape, else 0 (also for M outside 1..32). Host only; no GPU call.
+ * One launch when its per-token quantizing workgroups (the decode plan's waves)
+ * are at least as wide as the stand-alone quantizer's and M = 1, or M <= 16 with
+ * K >= 12288: where it measured faster on MI355X.
+ */
+int mq_act_one_launch(int64_t M, int64_t N, int64_t K);
 int mq_gemm_w4a4_residual_act(const void* x, int x_dtype, const uint8_t* wq, const uint16_t* sw,
                               const int32_t* rmap, const uint8_t* rq, int64_t nnz, int64_t M,
                               int64_t N, int64_t K, int group, int bn, int bk, uint8_t* xq,

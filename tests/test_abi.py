@@ -155,8 +155,10 @@ def test_preparation_calls_reject_bad_arguments(lib_nogpu):
     assert act(sync=FAKE + 2) == -1
     assert act(launch=3) == -1 and act(launch=-1) == -1
     assert act(M=33) == -1, "one launch takes at most 32 tokens"
-    # "auto" takes one launch at M <= 4 over N <= 5120 columns: then the counters are required
-    assert act(launch=0, M=4, K=512, sync=None) == -1
+    # "auto" takes one launch for one token of 8192 inputs over 512 columns (16-wave
+    # producers): then the counters are required
+    assert lib.mq_act_one_launch(1, 512, 8192) == 1
+    assert act(launch=0, M=1, K=8192, sync=None) == -1
     assert act(M=0, x=None, sync=None) == 0
 
 
@@ -170,24 +172,27 @@ def test_read_probe_rejections(lib_nogpu):
 
 
 def test_act_launch_rule(mq):
-    """The binding's copy of the library's "auto" rule for the self-quantizing GEMM
-    (one launch iff M <= 32, N <= 5120, and M <= 4 or K >= 12288), on shapes it was
-    measured on, and the header's constants as the binding uses them."""
+    """The library's "auto" rule for the self-quantizing GEMM (mq_act_one_launch, a
+    host function), on shapes where it was measured, and the header's constants as
+    the binding uses them."""
     txt = open(HEADER).read()
     defs = dict(re.findall(r"#define (MQ_[A-Z_]+) (\d+)", txt))
     assert int(defs["MQ_SYNC_WORDS"]) == mq.SYNC_WORDS
     assert [int(defs[k]) for k in ("MQ_ACT_AUTO", "MQ_ACT_ONE_LAUNCH", "MQ_ACT_TWO_LAUNCHES")] == \
         [mq._ACT_LAUNCH[k] for k in ("auto", "one", "two")]
-    rule = mq.act_one_launch
-    # down projections of 8B / 32B models (K >= 12288, N <= 5120): one launch at every M
-    assert rule(1, 4096, 14336) and rule(32, 4096, 14336) and rule(32, 5120, 25600)
-    # short rows over few columns: one launch only for M <= 4
-    assert rule(4, 1024, 4096) and rule(4, 5120, 5120) and not rule(5, 4096, 4096)
-    assert not rule(16, 1024, 4096) and not rule(32, 1024, 8192)
-    # many columns (N > 5120): two launches, however long the rows
-    assert not rule(1, 14336, 4096) and not rule(1, 8192, 28672) and not rule(1, 12288, 12288)
-    assert not rule(33, 1, 1 << 20), "one launch takes at most 32 tokens"
-    assert rule(64, 1, 1, "one") and not rule(1, 1, 1 << 20, "two")
+    rule = mq.act_one_launch   # (M, N, K)
+    # one token over up to 5120 columns: one launch (its producers are as wide as
+    # the stand-alone quantizer)
+    assert rule(1, 1024, 4096) and rule(1, 4096, 4096) and rule(1, 5120, 5120)
+    # long rows over up to 4096 columns (16-wave producers): one launch up to 16 tokens
+    assert rule(4, 4096, 14336) and rule(16, 4096, 14336) and not rule(32, 4096, 14336)
+    # short rows: two launches from 4 tokens on
+    assert not rule(4, 4096, 4096) and not rule(8, 5120, 5120) and not rule(16, 1024, 4096)
+    # producers narrower than the stand-alone quantizer: two launches at any M
+    assert not rule(1, 5120, 25600) and not rule(1, 8192, 28672) and not rule(1, 14336, 4096)
+    assert not rule(1, 12288, 12288) and not rule(1, 28672, 8192)
+    assert not rule(33, 16, 1 << 16) and not rule(0, 4096, 4096), "one launch takes 1..32 tokens"
+    assert rule(64, 1, 1, "one") and not rule(1, 1024, 4096, "two")
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
