@@ -255,6 +255,10 @@ EDGE = [
     synth.custom_config("m33_tiled_small", M=33, K=256, N=128, bn=64, x_dist="t3"),
     # long K: one wavefront per 4 groups up to 16, plus uneven splits
     synth.custom_config("long_k", M=8, K=128 * 75, N=128, bn=64),
+    # residual walks after the K loop over tables of more than 64 column blocks
+    # (several ballot chunks): the one-row-tile (mid-size) and three-row-tile kernels
+    synth.custom_config("mid_long_k", M=64, K=128 * 72, N=256, bn=64),
+    synth.custom_config("wide_long_k", M=400, K=128 * 70, N=256, bn=128),
 ]
 
 
