@@ -198,6 +198,10 @@ def bench_variants(mq, torch, layer, k_blocks, calls, bf16=True):
         out[name] = _graph_time_us(torch, fn, calls)
         if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
             raise RuntimeError(f"graph replay of the {name} GEMM differs from the eager call")
+    # dense and fused again, after the other legs: the first graph a process times can
+    # run while the clocks ramp, so each of the two reports the better of its passes
+    for name, fn in legs[:2]:
+        out[name] = min(out[name], _graph_time_us(torch, fn, calls))
     out["act_auto_one"] = 1.0 if mq.act_one_launch(cfg.M, cfg.N, cfg.K) else 0.0
     del sets
     if bf16:
