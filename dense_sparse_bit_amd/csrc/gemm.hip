@@ -749,21 +749,28 @@ __global__ __launch_bounds__(64 * NWN, DUMP ? 1 : 2) void k_gemm_wide(GemmArgs a
                 __builtin_amdgcn_wave_barrier();
                 n += __builtin_popcountll(chosen);
             }
+            // (the fetch is unconditional, of the last entry again past the end: a
+            // fetch under a branch would leave the compiler unsure how many loads are
+            // in flight at the join, and it would wait for all of them)
             TailOps t0, t1;
-            if (n > 0) tail_fetch(__builtin_amdgcn_readfirstlane(wt[0]), t0);
-            for (int q = 0; q < n; q += 2) {
-                if (q + 1 < n) tail_fetch(__builtin_amdgcn_readfirstlane(wt[q + 1]), t1);
-                tail_mul(t0);
-                if (q + 1 >= n) break;
-                if (q + 2 < n) tail_fetch(__builtin_amdgcn_readfirstlane(wt[q + 2]), t0);
-                tail_mul(t1);
+            if (n > 0) {
+                tail_fetch(__builtin_amdgcn_readfirstlane(wt[0]), t0);
+                for (int q = 0;; q += 2) {
+                    tail_fetch(__builtin_amdgcn_readfirstlane(wt[min(q + 1, n - 1)]), t1);
+                    tail_mul(t0);
+                    if (q + 1 >= n) break;
+                    tail_fetch(__builtin_amdgcn_readfirstlane(wt[min(q + 2, n - 1)]), t0);
+                    tail_mul(t1);
+                    if (q + 2 >= n) break;
+                }
             }
         } else {
-            // three row tiles: a second set of operands in flight spills (measured
-            // slower), and so did fetching all of a block's operands before its
-            // products (210.3 against 206.3 us on the Qwen3-14B prefill shape): the
-            // scales and codes go first, each row tile's activations just before its
-            // MFMAs; the chosen entries of each 64-entry chunk come from one ballot
+            // three row tiles: the next block's operands fetched while one is
+            // multiplied measured no faster here (206.9 against 207.2 us on the
+            // Qwen3-14B prefill shape; a wave's walk overlaps the other workgroup's K
+            // loop), so each block's scales and codes go first and each row tile's
+            // activations just before its MFMAs; the chosen entries of each 64-entry
+            // chunk come from one ballot
             for (int c0 = 0; c0 < nbc; c0 += 64) {
                 const int v = c0 + lane < nbc ? wt[c0 + lane] : -1;
                 uint64_t chosen = __ballot(v >= 0);
