@@ -254,6 +254,83 @@ __device__ __forceinline__ bool spin_until(const int* p, int target, int* gave_u
     return true;
 }
 
+// The protocol's three parts.
+// Producer: the calling workgroup (every thread) quantizes token tok and counts it.
+__device__ __forceinline__ void qx_produce(const GemmArgs& a, int tok, int tid, float* qred,
+                                           uint8_t (*qfix)[8 * kQaWords]) {
+    quant_act_row(a.x, a.x_bf16, a.M, a.K, nullptr, a.xq_w, a.sx_w, tok, tid, blockDim.x, qred, qfix);
+    // each wave's stores have reached its XCD's L2 before the barrier; the count's
+    // device-scope release then writes that L2 back
+    wait_all_memory();
+    __syncthreads();
+    if (tid == 0) __hip_atomic_fetch_add(&a.sync[kSyncCount], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Column workgroup ci (dispatch order) of C, thread 0 only: returns once every
+// token is counted and this XCD's L2 holds no stale activations. The caller then
+// holds the workgroup at a barrier before its first activation load.
+__device__ __forceinline__ void qx_wait(int* sy, int M, int ci, int C) {
+    int* const gave_up = &sy[kSyncGaveUp];
+    const int L = min(kSyncSlots, C);
+    // XCC id: hardware register 20, bits 3:0 (uniform over the workgroup)
+    const int xcc = static_cast<int>(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20)) & (kSyncSlots - 1);
+    int* const ready = &sync_slot(sy, xcc)[kSyncReady];
+    if (ci < L) {
+        spin_until(&sy[kSyncCount], M, gave_up);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // this XCD's L2 holds no stale activations
+        __hip_atomic_store(ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wait_all_memory();   // the flag is up before the check-in
+        __hip_atomic_fetch_add(&sy[kSyncLeaders], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        bool up = false;
+        for (int it = 0;; ++it) {
+            if (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { up = true; break; }
+            if (__hip_atomic_load(&sy[kSyncLeaders], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= L) break;
+            if (it >= kSpinLimit) {
+                __hip_atomic_store(gave_up, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+        // every leader has checked in, so every flag that will be raised is up
+        if (!up && !__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no leader ran on this XCD
+    }
+}
+
+// Column workgroup ci of C, thread 0 only, after its last use of the counters:
+// counts itself done; the last one waits for the others and clears the words.
+__device__ __forceinline__ void qx_done(int* sy, int ci, int C) {
+    // A follower's accesses to the words were loads whose values it has used, so
+    // they are complete; a leader's check-in must land before its done count, so
+    // it waits (for its output stores too: 16 workgroups only).
+    if (ci < min(kSyncSlots, C)) wait_all_memory();
+    if (ci < C - 1) {
+        __hip_atomic_fetch_add(&sync_slot(sy, ci & (kSyncSlots - 1))[kSyncDone], 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        // the last column workgroup: every other one was dispatched before it and
+        // waits on nothing it holds, so their done counts all arrive
+        for (int it = 0;; ++it) {
+            int total = 0;
+            for (int i = 0; i < kSyncSlots; ++i)
+                total += __hip_atomic_load(&sync_slot(sy, i)[kSyncDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (total >= C - 1) break;
+            if (it >= kSpinLimit) {
+                __hip_atomic_store(&sy[kSyncGaveUp], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);   // the launch ends with this wait: poll closely
+        }
+        for (int i = 0; i < kSyncSlots; ++i) {
+            __hip_atomic_store(&sync_slot(sy, i)[kSyncReady], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&sync_slot(sy, i)[kSyncDone], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __hip_atomic_store(&sy[kSyncLeaders], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&sy[kSyncCount], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 template <int MT, bool RES, bool DUMP, int OUTMODE, bool QX = false>
 __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a) {
     // two groups per step; one for the residual variant with two row tiles,
@@ -268,12 +345,7 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
         __shared__ float qred[kQaMaxWaves];
         __shared__ uint8_t qfix[kQaMaxWaves][8 * kQaWords];
         if (static_cast<int>(blockIdx.x) < a.M) {
-            quant_act_row(a.x, a.x_bf16, a.M, a.K, nullptr, a.xq_w, a.sx_w, blockIdx.x, tid, blockDim.x, qred, qfix);
-            // each wave's stores have reached its XCD's L2 before the barrier; the
-            // count's device-scope release then writes that L2 back
-            wait_all_memory();
-            __syncthreads();
-            if (tid == 0) __hip_atomic_fetch_add(&a.sync[kSyncCount], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            qx_produce(a, blockIdx.x, tid, qred, qfix);
             return;
         }
     }
@@ -351,35 +423,7 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
             dec_fetch_main<MT, QS, false>(s1, src, gb + QS, lane);
             if (RES) dec_fetch_res<MT, QS, RES>(s1, a, src, tab, rrow, G, gb + QS, lane);
         }
-        if (tid == 0) {
-            int* const sy = a.sync;
-            int* const gave_up = &sy[kSyncGaveUp];
-            const int L = min(kSyncSlots, C);
-            // XCC id: hardware register 20, bits 3:0 (uniform over the workgroup)
-            const int xcc = static_cast<int>(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20)) & (kSyncSlots - 1);
-            int* const ready = &sync_slot(sy, xcc)[kSyncReady];
-            if (nt < L) {
-                spin_until(&sy[kSyncCount], a.M, gave_up);
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // this XCD's L2 holds no stale activations
-                __hip_atomic_store(ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                wait_all_memory();   // the flag is up before the check-in
-                __hip_atomic_fetch_add(&sy[kSyncLeaders], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-            } else {
-                bool up = false;
-                for (int it = 0;; ++it) {
-                    if (__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) { up = true; break; }
-                    if (__hip_atomic_load(&sy[kSyncLeaders], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= L) break;
-                    if (it >= kSpinLimit) {
-                        __hip_atomic_store(gave_up, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(8);
-                }
-                // every leader has checked in, so every flag that will be raised is up
-                if (!up && !__hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no leader ran on this XCD
-            }
-        }
+        if (tid == 0) qx_wait(a.sync, a.M, nt, C);
         __syncthreads();
         if (gb < ge) dec_fetch_x<MT, QS>(s0, src, gb);
         if (gb + QS < ge) dec_fetch_x<MT, QS>(s1, src, gb + QS);
@@ -410,37 +454,7 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
         const int m = t * 16 + (l >> 4) * 4 + r;
         if (m < a.M) store_out(a, OUTMODE, m, n0 + (l & 15), v);
     }
-    if (QX && tid == 0) {
-        int* const sy = a.sync;
-        // A follower's accesses to the words were loads whose values it has used, so
-        // they are complete; a leader's check-in must land before its done count, so
-        // it waits (for its output stores too: 16 workgroups only).
-        if (nt < min(kSyncSlots, C)) wait_all_memory();
-        if (nt < C - 1) {
-            __hip_atomic_fetch_add(&sync_slot(sy, nt & (kSyncSlots - 1))[kSyncDone], 1, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            // the last column workgroup: every other one was dispatched before it and
-            // waits on nothing it holds, so their done counts all arrive
-            for (int it = 0;; ++it) {
-                int total = 0;
-                for (int i = 0; i < kSyncSlots; ++i)
-                    total += __hip_atomic_load(&sync_slot(sy, i)[kSyncDone], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (total >= C - 1) break;
-                if (it >= kSpinLimit) {
-                    __hip_atomic_store(&sy[kSyncGaveUp], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);   // the launch ends with this wait: poll closely
-            }
-            for (int i = 0; i < kSyncSlots; ++i) {
-                __hip_atomic_store(&sync_slot(sy, i)[kSyncReady], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&sync_slot(sy, i)[kSyncDone], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            __hip_atomic_store(&sy[kSyncLeaders], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&sy[kSyncCount], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    if (QX && tid == 0) qx_done(a.sync, nt, C);
 }
 
 typedef float v16f __attribute__((ext_vector_type(16)));

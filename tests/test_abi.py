@@ -142,7 +142,7 @@ def test_preparation_calls_reject_bad_arguments(lib_nogpu):
     assert mapped(nnz=nb + 1) == -1
     assert mapped(K=320) == -2
     assert mapped(N=1 << 17, K=65536, bn=128, nnz=(1 << 31) // (128 * 32) + 1) == -2
-    # the self-quantizing GEMM: activations, map and (for M <= 32) the counters are required
+    # the self-quantizing GEMM: activations, map and (for one launch) the counters are required
     act = lambda **kw: lib.mq_gemm_w4a4_residual_act(
         kw.get("x", FAKE), kw.get("xd", 1), FAKE, FAKE, kw.get("rmap", FAKE), FAKE, 3, kw.get("M", 4),
         512, kw.get("K", 512), 128, 64, 64, FAKE, FAKE, kw.get("sync", FAKE), kw.get("launch", 1), FAKE, 1,

@@ -286,14 +286,15 @@ def test_degenerate_rows_and_groups(mq, orc):
     _check(mq, orc, inp, 7, "bf16")
 
 
-@pytest.mark.parametrize("launch", ["one", "two"])
-def test_self_quantizing_gemm_in_a_graph(mq, launch):
+@pytest.mark.parametrize("launch,M", [("one", 4), ("two", 4), ("two", 100), ("two", 400)])
+def test_self_quantizing_gemm_in_a_graph(mq, launch, M):
     """The self-quantizing GEMM captured in a HIP graph and replayed several times,
     with eager work and synchronizations between replays: every replay gives the
     eager call's y, codes and scales bit for bit, and (one launch) leaves its
-    counters zero, so replays need no clearing."""
+    counters zero, so replays need no clearing. M = 4 runs the decode kernel, 100
+    the prefill kernel's mid-size tile and 400 its large tile (two launches)."""
     import torch
-    cfg = synth.custom_config("graph_act", M=4, K=2048, N=512, bn=64)
+    cfg = synth.custom_config("graph_act", M=M, K=2048, N=512, bn=64)
     say(f"[graph] self-quantizing GEMM, launch={launch}, M={cfg.M} K={cfg.K} N={cfg.N}")
     inp = _inputs(cfg)
     x = torch.from_numpy(inp.X).cuda()
