@@ -720,7 +720,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        rows = args.cpu_rows or min(cfg.M, 128)
+        rows = args.cpu_rows or min(cfg.M, 256)
         log(f"[bench] CPU oracle baseline on {rows} tokens")
         cpu = cpu_baseline(cfg, inp, k_blocks, rows)
 
