@@ -276,7 +276,8 @@ static_assert(mq::kSyncWords == MQ_SYNC_WORDS, "sync array size");
 // weight loads: it was faster for one token, and for up to 16 tokens of rows of
 // at least 12288 inputs, and slower (or level) at more tokens.
 int mq_act_one_launch(int64_t M, int64_t N, int64_t K) {
-    if (M < 1 || M > 32 || N < 16 || K < mq::kGroup) return 0;
+    // outside the shapes the GEMM accepts (K <= 65536, M N < 2^31) there is no plan
+    if (M < 1 || M > 32 || N < 16 || K < mq::kGroup || K > 65536 || N > (int64_t(1) << 30)) return 0;
     if (64 * mq::plan_decode(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K)).nw <
         mq::quant_act_threads(M, K))
         return 0;

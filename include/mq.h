@@ -266,7 +266,8 @@ int mq_gemm_w4a4_residual_mapped(const uint8_t* xq, const float* sx, const uint8
 /*
  * The MQ_ACT_AUTO rule of mq_gemm_w4a4_residual_act, for callers that need to know
  * beforehand whether the counters are required: 1 if the call takes one launch
- * for this shape, else 0 (also for M outside 1..32). Host only; no GPU call.
+ * for this shape, else 0 (also for M outside 1..32, and for shapes the GEMM does
+ * not accept). Host only; no GPU call.
  * One launch when its per-token quantizing workgroups (the decode plan's waves)
  * are at least as wide as the stand-alone quantizer's and M = 1, or M <= 16 with
  * K >= 12288: where it measured faster on MI355X.

@@ -192,6 +192,7 @@ def test_act_launch_rule(mq):
     assert not rule(1, 5120, 25600) and not rule(1, 8192, 28672) and not rule(1, 14336, 4096)
     assert not rule(1, 12288, 12288) and not rule(1, 28672, 8192)
     assert not rule(33, 16, 1 << 16) and not rule(0, 4096, 4096), "one launch takes 1..32 tokens"
+    assert not rule(1, 1 << 40, 4096) and not rule(1, 4096, 1 << 40), "no plan outside the GEMM's shapes"
     assert rule(64, 1, 1, "one") and not rule(1, 1024, 4096, "two")
 
 
