@@ -82,29 +82,38 @@ struct DecSrc {
     int lo;                              // first CSR position of the block row
 };
 
-// base tiles, activations and scales of the step starting at group g0 (groups
-// past the last read zero through the range check)
+// Added to every offset of a step past the wave's groups: the loads fall outside
+// their buffers and read zero without touching memory. The step after the last is
+// fetched that way rather than skipped, so that no load depends on a branch: the
+// loads of a wave complete in issue order, and a load issued on one path only
+// would make the compiler wait for all of them before the next step's products.
+constexpr uint32_t kDeadStep = 0x80000000u;
+
+// activations of the step starting at group g0 (groups past the last read zero
+// through the range check)
 template <int MT, int QS>
-__device__ __forceinline__ void dec_fetch_x(DecStep<MT, QS>& st, const DecSrc& src, int g0) {
+__device__ __forceinline__ void dec_fetch_x(DecStep<MT, QS>& st, const DecSrc& src, int g0, uint32_t dead) {
 #pragma unroll
     for (int u = 0; u < QS; ++u)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) st.x[t][u] = buf_load16(src.x, (g0 + u) * src.xstride + src.xrow[t]);
+        for (int t = 0; t < MT; ++t) st.x[t][u] = buf_load16(src.x, ((g0 + u) * src.xstride + src.xrow[t]) | dead);
 }
 
-// X = false leaves the activations to a later dec_fetch_x
+// base tiles, activations and scales of the step starting at group g0; X = false
+// leaves the activations to a later dec_fetch_x
 template <int MT, int QS, bool X = true>
-__device__ __forceinline__ void dec_fetch_main(DecStep<MT, QS>& st, const DecSrc& src, int g0, int lane) {
+__device__ __forceinline__ void dec_fetch_main(DecStep<MT, QS>& st, const DecSrc& src, int g0, int lane,
+                                               uint32_t dead) {
 #pragma unroll
     for (int u = 0; u < QS; ++u) {
         const uint32_t g = g0 + u;
-        st.w[u] = buf_load16(src.w, g * 1024u + lane * 16u);
+        st.w[u] = buf_load16(src.w, (g * 1024u + lane * 16u) | dead);
         if (X) {
 #pragma unroll
-            for (int t = 0; t < MT; ++t) st.x[t][u] = buf_load16(src.x, g * src.xstride + src.xrow[t]);
+            for (int t = 0; t < MT; ++t) st.x[t][u] = buf_load16(src.x, (g * src.xstride + src.xrow[t]) | dead);
         }
     }
-    const uint32_t so = (g0 >> 2) * 128u + (lane & 15) * 8u + (g0 & 3) * 2u;
+    const uint32_t so = ((g0 >> 2) * 128u + (lane & 15) * 8u + (g0 & 3) * 2u) | dead;
     if (QS == 4) {
         const uint2 v = buf_load8(src.s, so);
         st.s[0] = v.x;
@@ -117,17 +126,18 @@ __device__ __forceinline__ void dec_fetch_main(DecStep<MT, QS>& st, const DecSrc
 }
 
 // residual rows of the step: the zipper table gives each column block's CSR
-// position (or -1); lanes 0-31 take the group's first block, 32-63 the second
+// position (or -1); lanes 0-31 take the group's first block, 32-63 the second.
+// Groups from ge on (past the wave's own) fetch none.
 template <int MT, int QS, bool RES>
 __device__ __forceinline__ void dec_fetch_res(DecStep<MT, QS>& st, const GemmArgs& a, const DecSrc& src,
-                                              const int* tab, int rrow, int G, int g0, int lane) {
+                                              const int* tab, int rrow, int ge, int g0, int lane) {
     const int kg = lane >> 4;
     st.rg = 0;
 #pragma unroll
     for (int u = 0; u < QS; ++u) {
         const int g = g0 + u;
         st.r[u] = make_uint4(0, 0, 0, 0);
-        if (RES && g < G) {
+        if (RES && g < ge) {
             // the table entry is the same for the whole wave: make that visible to
             // the compiler, so the residual branch in dec_compute is a scalar one
             const int j0 = __builtin_amdgcn_readfirstlane(tab[2 * g]);
@@ -147,13 +157,13 @@ __device__ __forceinline__ void dec_fetch_res(DecStep<MT, QS>& st, const GemmArg
 // chosen block in this block row adds the residual product Pr the same way and
 // forms T = 14 P + Pr (exact in fp32), dequantized with s_r = fp32(s / 14).
 template <int MT, int QS, bool RES, bool DUMP>
-__device__ __forceinline__ void dec_compute(const DecStep<MT, QS>& st, const GemmArgs& a, int n, int G, int g0,
-                                            int lane, float (&acc)[MT][4]) {
+__device__ __forceinline__ void dec_compute(const DecStep<MT, QS>& st, const GemmArgs& a, int n, int G, int ge,
+                                            int g0, int lane, float (&acc)[MT][4]) {
     const int kg = lane >> 4;
 #pragma unroll
     for (int u = 0; u < QS; ++u) {
         const int g = g0 + u;
-        if (g >= G) break;
+        if (g >= ge) break;
         const float sc = f16_bits_to_f32(static_cast<uint16_t>(st.s[u >> 1] >> (16 * (u & 1))));
         const bool res = RES && ((st.rg >> u) & 1);
         if (res) {
@@ -340,7 +350,11 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
     // launch so that a plan with few waves does not pay LDS (occupancy) for many
     extern __shared__ float red[];
     __shared__ int tab[RES ? 8 * (kMaxGroups / 4) : 1];   // column block -> CSR position
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    // the wave index as a scalar: the group loop's bounds and exits are then
+    // wave-uniform branches, not exec masks (a masked exit merges into the loop
+    // header and makes every load of the previous step look outstanding there)
+    const int tid = threadIdx.x, lane = tid & 63, nw = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (QX) {
         __shared__ float qred[kQaMaxWaves];
         __shared__ uint8_t qfix[kQaMaxWaves][8 * kQaWords];
@@ -393,7 +407,7 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
         const int kb0 = 2 * gb, kb1 = 2 * ge;
         int map0 = -1;
         if (RES && map) map0 = a.rmap[static_cast<int64_t>(br) * (2 * G) + min(kb0 + lane, kb1 - 1)];
-        dec_fetch_main<MT, QS, !QX>(s0, src, gb, lane);
+        dec_fetch_main<MT, QS, !QX>(s0, src, gb, lane, 0u);
         if (RES) {
             if (map) {
                 // out-of-range positions read as "no block"
@@ -413,33 +427,67 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
                 }
                 __builtin_amdgcn_wave_barrier();
             }
-            dec_fetch_res<MT, QS, RES>(s0, a, src, tab, rrow, G, gb, lane);
+            dec_fetch_res<MT, QS, RES>(s0, a, src, tab, rrow, ge, gb, lane);
         }
     }
     const int C = QX ? static_cast<int>(gridDim.x) - a.M : 0;   // column workgroups
     if (QX) {
         // the second step's weights, scales and residual rows go out before the wait too
-        if (gb + QS < ge) {
-            dec_fetch_main<MT, QS, false>(s1, src, gb + QS, lane);
-            if (RES) dec_fetch_res<MT, QS, RES>(s1, a, src, tab, rrow, G, gb + QS, lane);
+        if (gb < ge) {
+            const uint32_t d1 = gb + QS < ge ? 0u : kDeadStep;
+            dec_fetch_main<MT, QS, false>(s1, src, gb + QS, lane, d1);
+            if (RES) dec_fetch_res<MT, QS, RES>(s1, a, src, tab, rrow, ge, gb + QS, lane);
         }
         if (tid == 0) qx_wait(a.sync, a.M, nt, C);
         __syncthreads();
-        if (gb < ge) dec_fetch_x<MT, QS>(s0, src, gb);
-        if (gb + QS < ge) dec_fetch_x<MT, QS>(s1, src, gb + QS);
+        if (gb < ge) {
+            dec_fetch_x<MT, QS>(s0, src, gb, 0u);
+            dec_fetch_x<MT, QS>(s1, src, gb + QS, gb + QS < ge ? 0u : kDeadStep);
+        }
     }
-    for (int g = gb; g < ge; g += 2 * QS) {
-        if (g + QS < ge && !(QX && g == gb)) {   // (the self-quantizing variant fetched step 1 early)
-            dec_fetch_main<MT, QS>(s1, src, g + QS, lane);
-            if (RES) dec_fetch_res<MT, QS, RES>(s1, a, src, tab, rrow, G, g + QS, lane);
+    // Every fetch of the steady loop is for a step of the wave's own: no load is
+    // left to a branch inside it, and the loop has its one exit at the top (an
+    // exit between the halves would give the loop header a path on which the
+    // second half's loads were never issued). The last one or two steps follow
+    // it. s0 holds step g on entry to both.
+    int g = gb;
+    auto steady = [&]() {
+        for (; g + 2 * QS < ge; g += 2 * QS) {
+            dec_fetch_main<MT, QS>(s1, src, g + QS, lane, 0u);
+            if (RES) dec_fetch_res<MT, QS, RES>(s1, a, src, tab, rrow, ge, g + QS, lane);
+            dec_compute<MT, QS, RES, DUMP>(s0, a, n, G, ge, g, lane, acc);
+            dec_fetch_main<MT, QS>(s0, src, g + 2 * QS, lane, 0u);
+            if (RES) dec_fetch_res<MT, QS, RES>(s0, a, src, tab, rrow, ge, g + 2 * QS, lane);
+            // The residual kernel with two row tiles takes every load in before the
+            // second step of each pair (s_waitcnt vmcnt(0), expcnt and lgkmcnt left
+            // at their maxima): one step in flight at all times measured slower on
+            // the layers whose chosen blocks cluster in a few block rows.
+            if constexpr (RES && MT == 2) __builtin_amdgcn_s_waitcnt(0x0F70);
+            dec_compute<MT, QS, RES, DUMP>(s1, a, n, G, ge, g + QS, lane, acc);
         }
-        dec_compute<MT, QS, RES, DUMP>(s0, a, n, G, g, lane, acc);
-        if (g + QS >= ge) break;
-        if (g + 2 * QS < ge) {
-            dec_fetch_main<MT, QS>(s0, src, g + 2 * QS, lane);
-            if (RES) dec_fetch_res<MT, QS, RES>(s0, a, src, tab, rrow, G, g + 2 * QS, lane);
+        if (g + QS < ge) {
+            dec_fetch_main<MT, QS>(s1, src, g + QS, lane, 0u);
+            if (RES) dec_fetch_res<MT, QS, RES>(s1, a, src, tab, rrow, ge, g + QS, lane);
+            dec_compute<MT, QS, RES, DUMP>(s0, a, n, G, ge, g, lane, acc);
+            dec_compute<MT, QS, RES, DUMP>(s1, a, n, G, ge, g + QS, lane, acc);
+        } else if (g < ge) {
+            dec_compute<MT, QS, RES, DUMP>(s0, a, n, G, ge, g, lane, acc);
         }
-        dec_compute<MT, QS, RES, DUMP>(s1, a, n, G, g + QS, lane, acc);
+    };
+    if (!QX) {
+        steady();
+    } else if (g + 2 * QS < ge) {
+        // step 1 was fetched before the wait: the first two steps, then the loop
+        // (entered only here, so its header never sees step 1 unconsumed)
+        dec_compute<MT, QS, RES, DUMP>(s0, a, n, G, ge, g, lane, acc);
+        dec_fetch_main<MT, QS>(s0, src, g + 2 * QS, lane, 0u);
+        if (RES) dec_fetch_res<MT, QS, RES>(s0, a, src, tab, rrow, ge, g + 2 * QS, lane);
+        dec_compute<MT, QS, RES, DUMP>(s1, a, n, G, ge, g + QS, lane, acc);
+        g += 2 * QS;
+        steady();
+    } else if (g < ge) {
+        dec_compute<MT, QS, RES, DUMP>(s0, a, n, G, ge, g, lane, acc);
+        dec_compute<MT, QS, RES, DUMP>(s1, a, n, G, ge, g + QS, lane, acc);   // (nothing past ge)
     }
 
 #pragma unroll
