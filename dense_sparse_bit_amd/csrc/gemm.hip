@@ -938,12 +938,29 @@ __global__ __launch_bounds__(64 * NWN, DUMP ? 1 : 2) void k_gemm_wide(GemmArgs a
         schedule_step();
         __syncthreads();
     };
-    for (int g = 0; g < G; g += 3) {
-        step(g, B0, B2, S0, S2);
-        if (g + 1 >= G) break;
-        step(g + 1, B1, B0, S1, S0);
-        if (g + 2 >= G) break;
-        step(g + 2, B2, B1, S2, S1);
+    if constexpr (RES || kMT == 1) {
+        // one exit, at the top (an exit between steps would give the loop header a
+        // path on which the later steps' loads were never issued, and the compiler
+        // would wait there for every load in flight); the last one or two steps follow
+        int g = 0;
+        for (; g + 3 <= G; g += 3) {
+            step(g, B0, B2, S0, S2);
+            step(g + 1, B1, B0, S1, S0);
+            step(g + 2, B2, B1, S2, S1);
+        }
+        if (g < G) {
+            step(g, B0, B2, S0, S2);
+            if (g + 1 < G) step(g + 1, B1, B0, S1, S0);
+        }
+    } else {
+        // the dense-only wide tile: the two peeled steps above make it spill
+        for (int g = 0; g < G; g += 3) {
+            step(g, B0, B2, S0, S2);
+            if (g + 1 >= G) break;
+            step(g + 1, B1, B0, S1, S0);
+            if (g + 2 >= G) break;
+            step(g + 2, B2, B1, S2, S1);
+        }
     }
     if (RES) residual_blocks();
 
