@@ -57,19 +57,67 @@ __device__ __forceinline__ void quant_act_row(const void* __restrict__ x, int bf
     const int nw = nt >> 6;
     const void* row = bf16 ? static_cast<const void*>(static_cast<const uint16_t*>(x) + m * K)
                            : static_cast<const void*>(static_cast<const float*>(x) + m * K);
+    // The words kept in registers: every load is issued before the first is used
+    // (a load under a per-word branch would be waited for before the next word's
+    // went out). A word past the row reads the row's last word and is zeroed.
     float v[kQaWords][8];
     float a = 0.0f;
+    if (bf16) {
+        uint4 raw[kQaWords];
+#pragma unroll
+        for (int i = 0; i < kQaWords; ++i)
+            raw[i] = static_cast<const uint4*>(row)[min(t + static_cast<int64_t>(nt) * i, W - 1)];
+        __builtin_amdgcn_sched_barrier(0);   // all loads out before the first use
+#pragma unroll
+        for (int i = 0; i < kQaWords; ++i) {
+            const uint32_t p[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[i][2 * e] = __uint_as_float(p[e] << 16);
+                v[i][2 * e + 1] = __uint_as_float(p[e] & 0xffff0000u);
+            }
+        }
+    } else {
+        float4 ra[kQaWords], rb[kQaWords];
+#pragma unroll
+        for (int i = 0; i < kQaWords; ++i) {
+            const int64_t jc = min(t + static_cast<int64_t>(nt) * i, W - 1);
+            ra[i] = static_cast<const float4*>(row)[2 * jc];
+            rb[i] = static_cast<const float4*>(row)[2 * jc + 1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kQaWords; ++i) {
+            v[i][0] = ra[i].x; v[i][1] = ra[i].y; v[i][2] = ra[i].z; v[i][3] = ra[i].w;
+            v[i][4] = rb[i].x; v[i][5] = rb[i].y; v[i][6] = rb[i].z; v[i][7] = rb[i].w;
+        }
+    }
+    // migrated activations: x^ = fp32(x * r_k), one rounding per element
+    if (colscale) {
+        float4 ca[kQaWords], cb[kQaWords];
+#pragma unroll
+        for (int i = 0; i < kQaWords; ++i) {
+            const int64_t jc = min(t + static_cast<int64_t>(nt) * i, W - 1);
+            ca[i] = reinterpret_cast<const float4*>(colscale)[2 * jc];
+            cb[i] = reinterpret_cast<const float4*>(colscale)[2 * jc + 1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kQaWords; ++i) {
+            v[i][0] = v[i][0] * ca[i].x; v[i][1] = v[i][1] * ca[i].y;
+            v[i][2] = v[i][2] * ca[i].z; v[i][3] = v[i][3] * ca[i].w;
+            v[i][4] = v[i][4] * cb[i].x; v[i][5] = v[i][5] * cb[i].y;
+            v[i][6] = v[i][6] * cb[i].z; v[i][7] = v[i][7] * cb[i].w;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < kQaWords; ++i) {
-        const int64_t j = t + static_cast<int64_t>(nt) * i;
-        if (j < W) {
-            load8(row, bf16, j, v[i], colscale);
-        } else {
+        const bool in = t + static_cast<int64_t>(nt) * i < W;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+        for (int e = 0; e < 8; ++e) {
+            v[i][e] = in ? v[i][e] : 0.0f;
+            a = fmaxf(a, fabsf(v[i][e]));
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[i][e]));
     }
     for (int64_t j = t + static_cast<int64_t>(nt) * kQaWords; j < W; j += nt) {
         float u[8];
