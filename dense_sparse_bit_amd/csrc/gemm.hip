@@ -266,9 +266,8 @@ __device__ __forceinline__ bool spin_until(const int* p, int target, int* gave_u
 
 // The protocol's three parts.
 // Producer: the calling workgroup (every thread) quantizes token tok and counts it.
-__device__ __forceinline__ void qx_produce(const GemmArgs& a, int tok, int tid, float* qred,
-                                           uint8_t (*qfix)[8 * kQaWords]) {
-    quant_act_row(a.x, a.x_bf16, a.M, a.K, nullptr, a.xq_w, a.sx_w, tok, tid, blockDim.x, qred, qfix);
+__device__ __forceinline__ void qx_produce(const GemmArgs& a, int tok, int tid, float* qred) {
+    quant_act_row(a.x, a.x_bf16, a.M, a.K, nullptr, a.xq_w, a.sx_w, tok, tid, blockDim.x, qred);
     // each wave's stores have reached its XCD's L2 before the barrier; the count's
     // device-scope release then writes that L2 back
     wait_all_memory();
@@ -357,9 +356,8 @@ __global__ __launch_bounds__(64 * kMaxDecodeWaves) void k_gemm_decode(GemmArgs a
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (QX) {
         __shared__ float qred[kQaMaxWaves];
-        __shared__ uint8_t qfix[kQaMaxWaves][8 * kQaWords];
         if (static_cast<int>(blockIdx.x) < a.M) {
-            qx_produce(a, blockIdx.x, tid, qred, qfix);
+            qx_produce(a, blockIdx.x, tid, qred);
             return;
         }
     }

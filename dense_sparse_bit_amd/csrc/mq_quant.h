@@ -45,13 +45,11 @@ __device__ __forceinline__ void load8(const void* row, bool bf16, int64_t j, flo
 // consecutive inputs each) and keeps the first kQaWords of them in registers
 // between the exact max-reduction of |x| (order-free) and the quantization, so x
 // is read once for K <= 8 * kQaWords * nt. Words are stored group-major
-// ([K/128][M][64 B]), the layout the GEMM loads from. red: kQaMaxWaves floats,
-// fixb: kQaMaxWaves x 32 bytes of LDS. Contains workgroup barriers: every thread
-// of the workgroup must call it.
+// ([K/128][M][64 B]), the layout the GEMM loads from. red: kQaMaxWaves floats of
+// LDS. Contains workgroup barriers: every thread of the workgroup must call it.
 __device__ __forceinline__ void quant_act_row(const void* __restrict__ x, int bf16, int64_t M, int64_t K,
                                               const float* __restrict__ colscale, uint8_t* __restrict__ xq,
-                                              float* __restrict__ sx, int64_t m, int t, int nt, float* red,
-                                              uint8_t (*fixb)[8 * kQaWords]) {
+                                              float* __restrict__ sx, int64_t m, int t, int nt, float* red) {
 #pragma clang fp contract(off)
     const int64_t W = K / 8;
     const int nw = nt >> 6;
@@ -135,46 +133,34 @@ __device__ __forceinline__ void quant_act_row(const void* __restrict__ x, int bf
     if (t == 0) sx[m] = s;
     // group-major output: word j (inputs 8j..8j+7) is bytes 4(j%16).. of group j/16's chunk
     auto dst = [&](int64_t j) { return reinterpret_cast<uint32_t*>(xq + xq_row(j >> 4, M, m) + (j & 15) * 4); };
-    // branch-free codes for the values held in registers; rare near-ties (or a
-    // non-finite reciprocal) redo them with the exact quantizer
+    // Branch-free codes for the values held in registers. A quotient within 4e-6 of
+    // a rounding boundary (or any quotient, when 1/s is not finite: the products
+    // are then infinite or NaN and flag themselves) is marked in `near`, bit
+    // 8 i + e, and recoded exactly from the value still in its register.
+    static_assert(kQaWords * 8 <= 32, "one flag bit per register-held value");
     uint32_t nib[kQaWords];
-    float worst = 0.0f;
+    uint32_t near = 0;
 #pragma unroll
     for (int i = 0; i < kQaWords; ++i) {
         nib[i] = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            nib[i] |= (static_cast<uint32_t>(static_cast<int>(rtn_fast(v[i][e], rs, worst))) & 15u) << (4 * e);
+        for (int e = 0; e < 8; ++e) {
+            float worst = 0.0f;
+            const float c = rtn_fast(v[i][e], rs, worst);
+            near |= static_cast<uint32_t>(!(worst < kFastMargin)) << (8 * i + e);
+            nib[i] |= (static_cast<uint32_t>(static_cast<int>(c)) & 15u) << (4 * e);
+        }
     }
-    const bool redo = !(worst < kFastMargin) || !(fabsf(rs) <= 3.0e38f);
-    // Rare: a quotient within 4e-6 of a rounding boundary. The wave repairs each
-    // flagged lane L together: lane i < 32 recodes L's value i exactly, and L
-    // gathers the codes through LDS.
-    uint64_t flagged = __ballot(redo);
-    while (flagged) {
-        const int L = __builtin_ctzll(flagged);
-        flagged &= flagged - 1;
-        const int tL = (t & ~63) + L, l = t & 63;
-        if (l < 8 * kQaWords) {
-            const int64_t j = tL + static_cast<int64_t>(nt) * (l >> 3);
-            uint8_t c = 0;
-            if (j < W) {
-                float u[8];
-                load8(row, bf16, j, u, colscale);
-                c = static_cast<uint8_t>(static_cast<int>(rtn_codef(u[l & 7], s, rs)) & 15);
-            }
-            fixb[t >> 6][l] = c;
-        }
-        __builtin_amdgcn_wave_barrier();
-        if (l == L) {
+    if (!(fabsf(rs) <= 3.0e38f)) near = ~0u;
+    if (near) {
 #pragma unroll
-            for (int i = 0; i < kQaWords; ++i) {
-                nib[i] = 0;
+        for (int i = 0; i < kQaWords; ++i)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) nib[i] |= static_cast<uint32_t>(fixb[t >> 6][8 * i + e]) << (4 * e);
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
+            for (int e = 0; e < 8; ++e)
+                if ((near >> (8 * i + e)) & 1u) {
+                    const uint32_t c = static_cast<uint32_t>(static_cast<int>(rtn_codef(v[i][e], s, rs))) & 15u;
+                    nib[i] = (nib[i] & ~(15u << (4 * e))) | (c << (4 * e));
+                }
     }
 #pragma unroll
     for (int i = 0; i < kQaWords; ++i) {

@@ -75,8 +75,7 @@ __global__ __launch_bounds__(64 * kQaMaxWaves) void k_quant_act(const void* __re
                                                    const float* __restrict__ colscale,
                                                    uint8_t* __restrict__ xq, float* __restrict__ sx) {
     __shared__ float red[kQaMaxWaves];
-    __shared__ uint8_t fixb[kQaMaxWaves][8 * kQaWords];
-    quant_act_row(x, bf16, M, K, colscale, xq, sx, blockIdx.x, threadIdx.x, blockDim.x, red, fixb);
+    quant_act_row(x, bf16, M, K, colscale, xq, sx, blockIdx.x, threadIdx.x, blockDim.x, red);
 }
 
 // ---------------------------------------------------------------------------
