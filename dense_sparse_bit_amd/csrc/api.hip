@@ -281,7 +281,7 @@ int mq_act_one_launch(int64_t M, int64_t N, int64_t K) {
     if (64 * mq::plan_decode(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K)).nw <
         mq::quant_act_threads(M, K))
         return 0;
-    return (M == 1 || (M <= 16 && K >= 12288)) ? 1 : 0;
+    return (M == 1 && N >= 4096) ? 1 : 0;
 }
 
 int mq_gemm_w4a4_residual_act(const void* x, int x_dtype, const uint8_t* wq, const uint16_t* sw,

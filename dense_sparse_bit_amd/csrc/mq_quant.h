@@ -133,34 +133,32 @@ __device__ __forceinline__ void quant_act_row(const void* __restrict__ x, int bf
     if (t == 0) sx[m] = s;
     // group-major output: word j (inputs 8j..8j+7) is bytes 4(j%16).. of group j/16's chunk
     auto dst = [&](int64_t j) { return reinterpret_cast<uint32_t*>(xq + xq_row(j >> 4, M, m) + (j & 15) * 4); };
-    // Branch-free codes for the values held in registers. A quotient within 4e-6 of
-    // a rounding boundary (or any quotient, when 1/s is not finite: the products
-    // are then infinite or NaN and flag themselves) is marked in `near`, bit
-    // 8 i + e, and recoded exactly from the value still in its register.
-    static_assert(kQaWords * 8 <= 32, "one flag bit per register-held value");
+    // Branch-free codes for the values held in registers. A word with a quotient
+    // within 4e-6 of a rounding boundary (or every word, when 1/s is not finite:
+    // the products are then infinite or NaN and flag themselves) is marked in
+    // `near` and recoded exactly from the values still in its registers (a value
+    // that was not near a boundary gets the same code either way).
     uint32_t nib[kQaWords];
     uint32_t near = 0;
 #pragma unroll
     for (int i = 0; i < kQaWords; ++i) {
+        float worst = 0.0f;
         nib[i] = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float worst = 0.0f;
-            const float c = rtn_fast(v[i][e], rs, worst);
-            near |= static_cast<uint32_t>(!(worst < kFastMargin)) << (8 * i + e);
-            nib[i] |= (static_cast<uint32_t>(static_cast<int>(c)) & 15u) << (4 * e);
-        }
+        for (int e = 0; e < 8; ++e)
+            nib[i] |= (static_cast<uint32_t>(static_cast<int>(rtn_fast(v[i][e], rs, worst))) & 15u) << (4 * e);
+        near |= static_cast<uint32_t>(!(worst < kFastMargin)) << i;
     }
-    if (!(fabsf(rs) <= 3.0e38f)) near = ~0u;
+    if (!(fabsf(rs) <= 3.0e38f)) near = (1u << kQaWords) - 1u;
     if (near) {
 #pragma unroll
         for (int i = 0; i < kQaWords; ++i)
+            if ((near >> i) & 1u) {
+                nib[i] = 0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if ((near >> (8 * i + e)) & 1u) {
-                    const uint32_t c = static_cast<uint32_t>(static_cast<int>(rtn_codef(v[i][e], s, rs))) & 15u;
-                    nib[i] = (nib[i] & ~(15u << (4 * e))) | (c << (4 * e));
-                }
+                for (int e = 0; e < 8; ++e)
+                    nib[i] |= (static_cast<uint32_t>(static_cast<int>(rtn_codef(v[i][e], s, rs))) & 15u) << (4 * e);
+            }
     }
 #pragma unroll
     for (int i = 0; i < kQaWords; ++i) {

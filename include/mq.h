@@ -269,8 +269,8 @@ int mq_gemm_w4a4_residual_mapped(const uint8_t* xq, const float* sx, const uint8
  * for this shape, else 0 (also for M outside 1..32, and for shapes the GEMM does
  * not accept). Host only; no GPU call.
  * One launch when its per-token quantizing workgroups (the decode plan's waves)
- * are at least as wide as the stand-alone quantizer's and M = 1, or M <= 16 with
- * K >= 12288: where it measured faster on MI355X.
+ * are at least as wide as the stand-alone quantizer's, M = 1 and N >= 4096: where
+ * it measured faster on MI355X.
  */
 int mq_act_one_launch(int64_t M, int64_t N, int64_t K);
 int mq_gemm_w4a4_residual_act(const void* x, int x_dtype, const uint8_t* wq, const uint16_t* sw,

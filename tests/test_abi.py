@@ -145,8 +145,8 @@ def test_preparation_calls_reject_bad_arguments(lib_nogpu):
     # the self-quantizing GEMM: activations, map and (for one launch) the counters are required
     act = lambda **kw: lib.mq_gemm_w4a4_residual_act(
         kw.get("x", FAKE), kw.get("xd", 1), FAKE, FAKE, kw.get("rmap", FAKE), FAKE, 3, kw.get("M", 4),
-        512, kw.get("K", 512), 128, 64, 64, FAKE, FAKE, kw.get("sync", FAKE), kw.get("launch", 1), FAKE, 1,
-        None)
+        kw.get("N", 512), kw.get("K", 512), 128, 64, 64, FAKE, FAKE, kw.get("sync", FAKE), kw.get("launch", 1),
+        FAKE, 1, None)
     assert act(x=None) == -1
     assert act(x=FAKE + 8) == -1
     assert act(xd=5) == -1
@@ -155,10 +155,10 @@ def test_preparation_calls_reject_bad_arguments(lib_nogpu):
     assert act(sync=FAKE + 2) == -1
     assert act(launch=3) == -1 and act(launch=-1) == -1
     assert act(M=33) == -1, "one launch takes at most 32 tokens"
-    # "auto" takes one launch for one token of 8192 inputs over 512 columns (16-wave
+    # "auto" takes one launch for one token of 8192 inputs over 4096 columns (16-wave
     # producers): then the counters are required
-    assert lib.mq_act_one_launch(1, 512, 8192) == 1
-    assert act(launch=0, M=1, K=8192, sync=None) == -1
+    assert lib.mq_act_one_launch(1, 4096, 8192) == 1
+    assert act(launch=0, M=1, N=4096, K=8192, sync=None) == -1
     assert act(M=0, x=None, sync=None) == 0
 
 
@@ -181,12 +181,12 @@ def test_act_launch_rule(mq):
     assert [int(defs[k]) for k in ("MQ_ACT_AUTO", "MQ_ACT_ONE_LAUNCH", "MQ_ACT_TWO_LAUNCHES")] == \
         [mq._ACT_LAUNCH[k] for k in ("auto", "one", "two")]
     rule = mq.act_one_launch   # (M, N, K)
-    # one token over up to 5120 columns: one launch (its producers are as wide as
+    # one token over 4096 to 8192 columns: one launch (its producers are as wide as
     # the stand-alone quantizer)
-    assert rule(1, 1024, 4096) and rule(1, 4096, 4096) and rule(1, 5120, 5120)
-    # long rows over up to 4096 columns (16-wave producers): one launch up to 16 tokens
-    assert rule(4, 4096, 14336) and rule(16, 4096, 14336) and not rule(32, 4096, 14336)
-    # short rows: two launches from 4 tokens on
+    assert rule(1, 4096, 4096) and rule(1, 5120, 5120) and rule(1, 4096, 14336) and rule(1, 8192, 8192)
+    # narrow layers, and more than one token: two launches
+    assert not rule(1, 1024, 4096) and not rule(1, 1024, 8192)
+    assert not rule(4, 4096, 14336) and not rule(16, 4096, 14336) and not rule(32, 4096, 14336)
     assert not rule(4, 4096, 4096) and not rule(8, 5120, 5120) and not rule(16, 1024, 4096)
     # producers narrower than the stand-alone quantizer: two launches at any M
     assert not rule(1, 5120, 25600) and not rule(1, 8192, 28672) and not rule(1, 14336, 4096)
